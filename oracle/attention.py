@@ -1,0 +1,245 @@
+"""Plain-definition fp64 forward and backward ([RPA] §3, App. B.1).
+
+For one (batch, head) slice with queries q_i, keys k_j, values v_j the score is
+the unified additive form of [RPA] §3.2 Eq. (4), with the two Transformer-XL
+query biases written out as in the configurations' score formula:
+
+    S_ij = tau * ( (q_i + u) . k_j
+                   + (q_i + v) . A^Q[phi_Q(i, j)]
+                   + k_j . A^K[phi_K(i, j)]
+                   + b[phi_b(i, j)] )  + M_ij
+
+(absent terms are zero; M_ij = -inf for j > i under the causal mask).  Then
+P = softmax_row(S), O = P V and L_i = log sum_j exp(S_ij) ([RPA] §3.1 Eq. (1)).
+
+Backward ([RPA] App. B.1, the dV/dS lemma): dV = P^T dO, dP = dO V^T,
+D_i = <dO_i, O_i>, dS = P * (dP - D).  With G = tau * dS the relation
+gradients follow [RPA] §3.2 Eq. (6) (one row of dZ per pair, by map row) and
+the matrix products of the App. B.1 table-gradient lemma:
+
+    dZ^Q[i, r] = sum_{j: phi_Q(i,j) = r} G_ij      dQ = G K + dZ^Q A^Q
+    dZ^K[j, r] = sum_{i: phi_K(i,j) = r} G_ij      dK = G^T (Q + u) + dZ^K A^K
+    dA^Q = (dZ^Q)^T (Q + v)      dA^K = (dZ^K)^T K      db[r] = sum_{phi_b = r} G
+    du = sum_ij G_ij k_j         dv = sum_i (dZ^Q A^Q)_i
+
+Table gradients are summed over the batch (and over heads for a table shared
+by all heads).  Everything is float64.
+"""
+
+import numpy as np
+
+from .maps import map_rows, relation_rows
+
+
+def _has(spec, term):
+    return term in spec["terms"]
+
+
+def _aq(spec, arrays, h):
+    a = arrays["aq"]
+    return a if spec["aq_shared"] else a[:, h, :]
+
+
+def _rows(spec, term, rows):
+    """Cached relation rows of ``term``; masked (causal) pairs get row 0, which
+    they never contribute to (their P and dS are zero, [RPA] App. B.1)."""
+    if term not in rows:
+        rho = relation_rows(spec, term)
+        if spec["causal"]:
+            rho[np.triu_indices(spec["N"], 1)] = 0
+        rows[term] = rho
+    return rows[term]
+
+
+def slice_scores(spec, arrays, b, h, rows=None):
+    """Score matrix S (fp64, N x N) of slice (b, h), with the relation-row
+    matrices used to build it.  ``rows`` caches ``relation_rows`` results."""
+    N = spec["N"]
+    tau = float(spec["scale"])
+    q = arrays["q"][b, h]
+    k = arrays["k"][b, h]
+    rows = {} if rows is None else rows
+    qc = q + arrays["u"][h] if _has(spec, "u") else q
+    s = qc @ k.T
+    if _has(spec, "aq"):
+        _rows(spec, "aq", rows)
+        a = _aq(spec, arrays, h)
+        qp = q + arrays["v_bias"][h] if _has(spec, "v") else q
+        zfull = qp @ a.T  # [N, R]: Z^Q of Eq. (5), every row
+        s += np.take_along_axis(zfull, rows["aq"], axis=1)
+    if _has(spec, "ak"):
+        _rows(spec, "ak", rows)
+        a = arrays["ak"][:, h, :]
+        zfull = k @ a.T  # [N, R]: Z^K of Eq. (5)
+        # term (i, j) = Z^K[j, phi_K(i, j)]
+        s += np.take_along_axis(zfull.T, rows["ak"], axis=0)
+    if _has(spec, "bias"):
+        _rows(spec, "bias", rows)
+        s += arrays["bias"][:, h][rows["bias"]]
+    s *= tau
+    if spec["causal"]:
+        s[np.triu_indices(N, 1)] = -np.inf
+    return s, rows
+
+
+def slice_forward(spec, arrays, b, h, rows=None):
+    """O (N x d) and natural-log L (N) of slice (b, h) ([RPA] §3.1 Eq. (1))."""
+    s, rows = slice_scores(spec, arrays, b, h, rows)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    ssum = e.sum(axis=1, keepdims=True)
+    p = e / ssum
+    o = p @ arrays["v"][b, h]
+    lse = (m + np.log(ssum))[:, 0]
+    return o, lse, p, rows
+
+
+def slice_forward_backward(spec, arrays, b, h, rows=None):
+    """Forward and backward of one slice.  Returns a dict with o, lse, dq, dk,
+    dv and this slice's contributions to the table gradients."""
+    tau = float(spec["scale"])
+    o, lse, p, rows = slice_forward(spec, arrays, b, h, rows)
+    q = arrays["q"][b, h]
+    k = arrays["k"][b, h]
+    v = arrays["v"][b, h]
+    do = arrays["do"][b, h]
+    N = spec["N"]
+    R = spec.get("rows", 0)
+    out = {"o": o, "lse": lse}
+    out["dv"] = p.T @ do                       # dV = P^T dO
+    dp = do @ v.T                              # dP = dO V^T
+    dd = np.sum(do * o, axis=1, keepdims=True)  # D_i = <dO_i, O_i>
+    ds = p * (dp - dd)                         # dS = P * (dP - D)
+    g = tau * ds                               # every term of S carries tau
+    del p, dp, ds
+    dq = g @ k
+    kc = k
+    dk = g.T @ (q + arrays["u"][h] if _has(spec, "u") else q)
+    if _has(spec, "u"):
+        out["du"] = g.sum(axis=0) @ kc           # sum_ij G_ij k_j
+    if _has(spec, "aq"):
+        a = _aq(spec, arrays, h)
+        # Eq. (6): dZ^Q[i, r] = sum over j with phi_Q(i, j) = r of G_ij
+        flat = (np.arange(N)[:, None] * R + rows["aq"]).ravel()
+        dzq = np.bincount(flat, weights=g.ravel(), minlength=N * R).reshape(N, R)
+        qp = q + arrays["v_bias"][h] if _has(spec, "v") else q
+        dq += dzq @ a
+        out["daq"] = dzq.T @ qp
+        if _has(spec, "v"):
+            out["dv_bias"] = dzq.sum(axis=0) @ a
+    if _has(spec, "ak"):
+        a = arrays["ak"][:, h, :]
+        # Eq. (6): dZ^K[j, r] = sum over i with phi_K(i, j) = r of G_ij
+        flat = (np.arange(N)[None, :] * R + rows["ak"]).ravel()
+        dzk = np.bincount(flat, weights=g.ravel(), minlength=N * R).reshape(N, R)
+        dk += dzk @ a
+        out["dak"] = dzk.T @ k
+    if _has(spec, "bias"):
+        out["dbias"] = np.bincount(rows["bias"].ravel(), weights=g.ravel(), minlength=R)
+    out["dq"] = dq
+    out["dk"] = dk
+    return out
+
+
+def _empty_grads(spec):
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    R = spec.get("rows", 0)
+    z = {"o": np.zeros((B, H, N, d)), "lse": np.zeros((B, H, N)),
+         "dq": np.zeros((B, H, N, d)), "dk": np.zeros((B, H, N, d)),
+         "dv": np.zeros((B, H, N, d))}
+    if _has(spec, "aq"):
+        z["daq"] = np.zeros((R, d)) if spec["aq_shared"] else np.zeros((R, H, d))
+    if _has(spec, "ak"):
+        z["dak"] = np.zeros((R, H, d))
+    if _has(spec, "bias"):
+        z["dbias"] = np.zeros((R, H))
+    if _has(spec, "u"):
+        z["du"] = np.zeros((H, d))
+    if _has(spec, "v"):
+        z["dv_bias"] = np.zeros((H, d))
+    return z
+
+
+def forward_backward(spec, arrays, heads=None, batches=None):
+    """Full forward + backward over the slices (b in ``batches``, h in ``heads``;
+    default all).  Returns full-shape arrays; slices not computed stay zero, and
+    table gradients hold only the computed slices' contributions."""
+    heads = range(spec["H"]) if heads is None else heads
+    batches = range(spec["B"]) if batches is None else batches
+    res = _empty_grads(spec)
+    rows = {}
+    for h in heads:
+        for b in batches:
+            r = slice_forward_backward(spec, arrays, b, h, rows)
+            for key in ("o", "lse", "dq", "dk", "dv"):
+                res[key][b, h] = r[key]
+            if "daq" in r:
+                if spec["aq_shared"]:
+                    res["daq"] += r["daq"]
+                else:
+                    res["daq"][:, h] += r["daq"]
+            if "dak" in r:
+                res["dak"][:, h] += r["dak"]
+            if "dbias" in r:
+                res["dbias"][:, h] += r["dbias"]
+            if "du" in r:
+                res["du"][h] += r["du"]
+            if "dv_bias" in r:
+                res["dv_bias"][h] += r["dv_bias"]
+    return res
+
+
+def forward(spec, arrays):
+    """O [B,H,N,d] and L [B,H,N] (natural log)."""
+    B, H = spec["B"], spec["H"]
+    o = np.zeros((B, H, spec["N"], spec["d"]))
+    lse = np.zeros((B, H, spec["N"]))
+    rows = {}
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h], _, rows = slice_forward(spec, arrays, b, h, rows)
+    return o, lse
+
+
+def backward(spec, arrays):
+    """All gradients (recomputes the forward; the oracle keeps nothing)."""
+    res = forward_backward(spec, arrays)
+    return {key: val for key, val in res.items() if key not in ("o", "lse")}
+
+
+def query_rows_forward(spec, arrays, b, h, rows_idx):
+    """O and L for selected query rows only, at O(len(rows_idx) * N * d) cost.
+
+    Used to check outputs at sizes where the full N x N matrix is too large to
+    revisit for every slice.  Same definition as ``slice_forward``.
+    """
+    N = spec["N"]
+    tau = float(spec["scale"])
+    ii = np.asarray(rows_idx, dtype=np.int64)
+    q = arrays["q"][b, h][ii]
+    k = arrays["k"][b, h]
+    jj = np.arange(N, dtype=np.int64)
+    delta = ii[:, None] - jj[None, :]
+    if spec["causal"]:
+        delta = np.maximum(delta, 0)  # masked pairs: any valid row, never used
+    s = (q + arrays["u"][h] if _has(spec, "u") else q) @ k.T
+    if _has(spec, "aq"):
+        a = _aq(spec, arrays, h)
+        qp = q + arrays["v_bias"][h] if _has(spec, "v") else q
+        rq = map_rows(spec["map"], spec["signs"]["aq"] * delta)
+        s += np.einsum("nd,njd->nj", qp, a[rq])
+    if _has(spec, "ak"):
+        a = arrays["ak"][:, h, :]
+        rk = map_rows(spec["map"], spec["signs"]["ak"] * delta)
+        s += np.einsum("jd,njd->nj", k, a[rk])
+    if _has(spec, "bias"):
+        rb = map_rows(spec["map"], spec["signs"]["bias"] * delta)
+        s += arrays["bias"][:, h][rb]
+    s *= tau
+    if spec["causal"]:
+        s[jj[None, :] > ii[:, None]] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    ssum = e.sum(axis=1, keepdims=True)
+    o = (e / ssum) @ arrays["v"][b, h]
+    return o, (m + np.log(ssum))[:, 0]
