@@ -1,0 +1,638 @@
+// C ABI of the library (include/relpos.h): validation, buffer carving and
+// the launch sequence of each entry point on the caller's stream.
+// [RPA] = "Fast and Exact Relative-Position Attention via Structure-Aware
+// Kernels" (arXiv 2611.01182), Table 9 gives the kernel order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "relpos.h"
+
+namespace relpos {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& detail) {
+  g_last_error = detail;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <typename P>
+P* at_off(void* base, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(base) + off);
+}
+
+#define RP_HIP(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(RELPOS_E_HIP, std::string(#expr) + ": " +        \
+                                                        hipGetErrorString(e_));        \
+  } while (0)
+
+struct ZView {
+  void* zq;
+  void* zk;
+  float *rowlo, *rowhi, *keylo, *keyhi, *keymid, *bt;
+};
+
+ZView z_view(const Plan& p, void* z) {
+  ZView v;
+  v.zq = p.aq ? at_off<char>(z, p.z_zq) : nullptr;
+  v.zk = p.ak ? at_off<char>(z, p.z_zk) : nullptr;
+  v.rowlo = at_off<float>(z, p.z_rowlo);
+  v.rowhi = at_off<float>(z, p.z_rowhi);
+  v.keylo = at_off<float>(z, p.z_keylo);
+  v.keyhi = at_off<float>(z, p.z_keyhi);
+  v.keymid = at_off<float>(z, p.z_keymid);
+  v.bt = at_off<float>(z, p.z_bt);
+  return v;
+}
+
+int check_inputs(const Plan& p, const relpos_tensors* in) {
+  if (in == nullptr) return fail(RELPOS_E_INVALID_ARG, "null tensors");
+  if (!in->q || !in->k || !in->v) return fail(RELPOS_E_INVALID_ARG, "null q, k or v");
+  if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v))
+    return fail(RELPOS_E_MISALIGNED, "q, k, v must be 16-byte aligned");
+  if (p.aq && (!in->aq || !aligned16(in->aq)))
+    return fail(in->aq ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG, "A^Q missing or misaligned");
+  if (p.ak && (!in->ak || !aligned16(in->ak)))
+    return fail(in->ak ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG, "A^K missing or misaligned");
+  if (p.bias && !in->bias) return fail(RELPOS_E_INVALID_ARG, "bias missing");
+  if (p.u && !in->u) return fail(RELPOS_E_INVALID_ARG, "u missing");
+  if (p.v && !in->vbias) return fail(RELPOS_E_INVALID_ARG, "v missing");
+  return RELPOS_OK;
+}
+
+// Group tables, expanded row maps and fold intervals, built on the device.
+int build_meta(const Plan& p, void* ws, hipStream_t s) {
+  MetaArgs m;
+  m.gq = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
+  m.gk = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+  m.N = p.N;
+  m.NG = p.NG;
+  m.D = p.delta;
+  m.causal = p.causal;
+  if (m.gq || m.gk) RP_HIP(launch_meta_groups(m, s));
+  struct Tab {
+    bool on;
+    const std::vector<int32_t>* beta;
+    size_t beta_off;
+    int sign;
+    int fold_idx;
+  } tabs[3] = {{p.aq, &p.beta_q, p.ws_beta_q, p.sign_q, 0},
+               {p.ak, &p.beta_k, p.ws_beta_k, p.sign_k, 1},
+               {p.bias, &p.beta_b, p.ws_beta_b, p.sign_b, 2}};
+  const int R = std::max(p.R, 1);
+  for (auto& t : tabs) {
+    if (!t.on) continue;
+    int32_t* beta = at_off<int32_t>(ws, t.beta_off);
+    if (p.affine_map) {
+      AffineMapArgs a;
+      a.beta = beta;
+      a.kind = p.map_kind;
+      a.sign = t.sign;
+      a.offset = p.map_offset;
+      a.clip = p.map_clip;
+      a.D = p.delta;
+      a.S = p.S;
+      a.R = R;
+      a.causal = p.causal;
+      RP_HIP(launch_meta_affine(a, s));
+    } else {
+      // bucketed / explicit maps: the host-built rows travel as kernel
+      // arguments (no host-to-device copy)
+      for (int k0 = 0; k0 < p.S; k0 += kMetaChunk) {
+        MetaChunk c;
+        c.dst = beta + k0;
+        c.count = std::min(kMetaChunk, p.S - k0);
+        std::memcpy(c.vals, t.beta->data() + k0, sizeof(int32_t) * c.count);
+        RP_HIP(launch_meta_fill(c, s));
+      }
+    }
+    int32_t* fold = at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(t.fold_idx) * R * 2;
+    RP_HIP(launch_fold_meta(beta, fold, p.S, R, s));
+  }
+  return RELPOS_OK;
+}
+
+const int32_t* fold_ptr(const Plan& p, void* ws, int idx) {
+  return at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(idx) * std::max(p.R, 1) * 2;
+}
+
+int expand_tables(const Plan& p, const relpos_desc* desc, const relpos_tensors* in, void* ws,
+                  hipStream_t s) {
+  const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
+  if (p.aq) {
+    ExpandArgs e;
+    e.table = in->aq;
+    e.row_stride = desc->aq_row_stride;
+    e.head_stride = desc->aq_head_stride;
+    e.beta = at_off<int32_t>(ws, p.ws_beta_q);
+    e.out = at_off<char>(ws, p.ws_atq);
+    e.Ht = p.Htq;
+    e.S = p.S;
+    RP_HIP(launch_expand(dt, e, s));
+  }
+  if (p.ak) {
+    ExpandArgs e;
+    e.table = in->ak;
+    e.row_stride = desc->ak_row_stride;
+    e.head_stride = desc->ak_head_stride;
+    e.beta = at_off<int32_t>(ws, p.ws_beta_k);
+    e.out = at_off<char>(ws, p.ws_atk);
+    e.Ht = p.Htk;
+    e.S = p.S;
+    RP_HIP(launch_expand(dt, e, s));
+  }
+  return RELPOS_OK;
+}
+
+int max_pitch(const SideLayout& L) {
+  int m = 0;
+  for (const auto& g : L.groups) m = std::max(m, g.pitch);
+  return m;
+}
+
+// Projection into z: bias table, Z^Q, Z^K, boundary entries.  Needs the
+// metadata and the expanded tables in ws.
+int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* in, void* z,
+                 void* ws, hipStream_t s) {
+  const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
+  ZView zv = z_view(p, z);
+  BiasExpandArgs be;
+  be.bias = p.bias ? in->bias : nullptr;
+  be.row_stride = desc->bias_row_stride;
+  be.head_stride = desc->bias_head_stride;
+  be.beta_b = at_off<int32_t>(ws, p.ws_beta_b);
+  be.vb = p.v ? in->vbias : nullptr;
+  be.atq = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+  be.htq_shared = p.aq_shared;
+  be.bt = zv.bt;
+  be.H = p.H;
+  be.S = p.S;
+  RP_HIP(launch_bias_expand(dt, be, s));
+  if (p.aq) {
+    ProjectArgs pa;
+    pa.x = in->q;
+    pa.at = at_off<char>(ws, p.ws_atq);
+    pa.at_shared = p.aq_shared;
+    pa.bt = zv.bt;
+    pa.gi = at_off<GroupInfo>(ws, p.ws_gq);
+    pa.z = zv.zq;
+    pa.z_bh = p.zq.bh_elems;
+    pa.N = p.N;
+    pa.H = p.H;
+    pa.D = p.delta;
+    pa.S = p.S;
+    pa.NG = p.NG;
+    RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zq), s));
+  }
+  if (p.ak) {
+    ProjectArgs pa;
+    pa.x = in->k;
+    pa.at = at_off<char>(ws, p.ws_atk);
+    pa.at_shared = p.ak_shared;
+    pa.bt = nullptr;
+    pa.gi = at_off<GroupInfo>(ws, p.ws_gk);
+    pa.z = zv.zk;
+    pa.z_bh = p.zk.bh_elems;
+    pa.N = p.N;
+    pa.H = p.H;
+    pa.D = p.delta;
+    pa.S = p.S;
+    pa.NG = p.NG;
+    RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zk), s));
+  }
+  RowKeyArgs rk;
+  rk.q = in->q;
+  rk.k = in->k;
+  rk.atq = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+  rk.atk = p.ak ? at_off<char>(ws, p.ws_atk) : nullptr;
+  rk.atq_shared = p.aq_shared;
+  rk.atk_shared = p.ak_shared;
+  rk.bt = zv.bt;
+  rk.u = p.u ? in->u : nullptr;
+  rk.rowlo = zv.rowlo;
+  rk.rowhi = zv.rowhi;
+  rk.keylo = zv.keylo;
+  rk.keyhi = zv.keyhi;
+  rk.keymid = zv.keymid;
+  rk.N = p.N;
+  rk.H = p.H;
+  rk.S = p.S;
+  RP_HIP(launch_rowkey(dt, rk, p.BH, s));
+  return RELPOS_OK;
+}
+
+AttnArgs attn_args(const Plan& p, const relpos_tensors* in, void* z, void* ws) {
+  ZView zv = z_view(p, z);
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.zq = zv.zq;
+  a.zk = zv.zk;
+  a.zq_bh = p.aq ? p.zq.bh_elems : 0;
+  a.zk_bh = p.ak ? p.zk.bh_elems : 0;
+  a.gq = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
+  a.gk = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+  a.rowlo = zv.rowlo;
+  a.rowhi = zv.rowhi;
+  a.keylo = zv.keylo;
+  a.keyhi = zv.keyhi;
+  a.keymid = zv.keymid;
+  a.bt = zv.bt;
+  a.N = p.N;
+  a.H = p.H;
+  a.D = p.delta;
+  a.S = p.S;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
+  return a;
+}
+
+int base_flags(const Plan& p) {
+  int f = 0;
+  if (p.aq) f |= F_ZQ;
+  if (p.ak) f |= F_ZK;
+  if (p.bias && !p.aq) f |= F_BT;
+  if (p.causal) f |= F_CAUSAL;
+  return f;
+}
+
+int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+                void* z, size_t z_bytes, void* ws, size_t ws_bytes, hipStream_t s) {
+  Plan p;
+  std::string detail;
+  int rc = make_plan(desc, shape, p, detail);
+  if (rc != RELPOS_OK) return fail(rc, detail);
+  if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
+  if (z == nullptr || z_bytes < p.z_bytes) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "z too small");
+  if (ws == nullptr || ws_bytes < p.ws_fwd_end)
+    return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
+  if (!aligned16(z) || !aligned16(ws)) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
+  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
+  return project_into(p, desc, in, z, ws, s);
+}
+
+int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+            const void* zc, size_t z_bytes, void* o, float* lse, void* ws, size_t ws_bytes,
+            hipStream_t s) {
+  Plan p;
+  std::string detail;
+  int rc = make_plan(desc, shape, p, detail);
+  if (rc != RELPOS_OK) return fail(rc, detail);
+  if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
+  if (o == nullptr || lse == nullptr || !aligned16(o) || !aligned16(lse))
+    return fail(o && lse ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG, "o / lse");
+  void* z = const_cast<void*>(zc);
+  const size_t need = z ? p.ws_fwd_end : p.ws_fwd_end + p.z_bytes;
+  if (ws == nullptr || ws_bytes < need) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
+  if (z && z_bytes < p.z_bytes) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "z too small");
+  if (!aligned16(ws) || (z && !aligned16(z))) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
+  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if (z == nullptr) {
+    z = at_off<char>(ws, p.ws_fwd_end);
+    if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
+    if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
+  }
+  AttnArgs a = attn_args(p, in, z, ws);
+  a.o = o;
+  a.lse = lse;
+  RP_HIP(launch_attn_fwd(p.dtype == RELPOS_DTYPE_F32 ? 0 : 1, base_flags(p), a, p.B, s));
+  return RELPOS_OK;
+}
+
+int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+            const void* zc, size_t z_bytes, const void* o, const float* lse, const void* dout,
+            relpos_grads* gr, void* ws, size_t ws_bytes, hipStream_t s) {
+  Plan p;
+  std::string detail;
+  int rc = make_plan(desc, shape, p, detail);
+  if (rc != RELPOS_OK) return fail(rc, detail);
+  if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
+  if (!o || !lse || !dout || !gr) return fail(RELPOS_E_INVALID_ARG, "null o, lse, dout or grads");
+  if (!aligned16(o) || !aligned16(dout)) return fail(RELPOS_E_MISALIGNED, "o / dout misaligned");
+  if (!gr->dq || !gr->dk || !gr->dv) return fail(RELPOS_E_INVALID_ARG, "null dq, dk or dv");
+  if (!aligned16(gr->dq) || !aligned16(gr->dk) || !aligned16(gr->dv))
+    return fail(RELPOS_E_MISALIGNED, "dq, dk, dv misaligned");
+  if ((p.aq && !gr->daq) || (p.ak && !gr->dak) || (p.bias && !gr->dbias) || (p.u && !gr->du) ||
+      (p.v && !gr->dvbias))
+    return fail(RELPOS_E_INVALID_ARG, "a table gradient pointer is null");
+  void* z = const_cast<void*>(zc);
+  const size_t need = z ? p.ws_bwd_end : p.ws_bwd_end + p.z_bytes;
+  if (ws == nullptr || ws_bytes < need) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
+  if (z && z_bytes < p.z_bytes) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "z too small");
+  if (!aligned16(ws) || (z && !aligned16(z))) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
+
+  const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
+  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
+  if (z == nullptr) {
+    z = at_off<char>(ws, p.ws_bwd_end);
+    if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
+  }
+  float* dvec = at_off<float>(ws, p.ws_D);
+  float* dqacc = at_off<float>(ws, p.ws_dqacc);
+  float* dkacc = at_off<float>(ws, p.ws_dkacc);
+  void* dz = at_off<char>(ws, p.ws_dz);
+  float* bndq = at_off<float>(ws, p.ws_bndq);
+  float* bndk = at_off<float>(ws, p.ws_bndk);
+  float* colsum = at_off<float>(ws, p.ws_colsum);
+  float* p1 = at_off<float>(ws, p.ws_p1);
+  float* p2 = at_off<float>(ws, p.ws_p2);
+  const int64_t rows = static_cast<int64_t>(p.BH) * p.N;
+
+  // Preprocessing: D = rowdot(dO, O)
+  RP_HIP(launch_rowdot(dt, p.out_dtype == RELPOS_DTYPE_F32, o, dout, dvec, rows, s));
+
+  AttnArgs a = attn_args(p, in, z, ws);
+  a.dout = dout;
+  a.o = const_cast<void*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.dvec = dvec;
+  a.dqacc = dqacc;
+  a.dkacc = dkacc;
+  a.dv = gr->dv;
+  a.dz = dz;
+  a.dz_bh = std::max(p.need_qside ? p.zq.bh_elems : 0, p.ak ? p.zk.bh_elems : 0);
+  a.bndq = bndq;
+  a.bndk = bndk;
+  a.colsum = colsum;
+  const int bf = base_flags(p);
+
+  // Query-parallel pass, then the query reduction ([RPA] Table 9)
+  RP_HIP(launch_attn_bwd_q(dt, bf | (p.need_qside ? F_DZQ : 0), a, p.B, s));
+  {
+    FinalizeArgs f;
+    std::memset(&f, 0, sizeof f);
+    f.acc = dqacc;
+    f.dz = p.aq ? dz : nullptr;
+    f.dz_bh = a.dz_bh;
+    f.gi = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
+    f.bnd = p.aq ? bndq : nullptr;
+    f.at = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+    f.at_shared = p.aq_shared;
+    f.out = gr->dq;
+    f.N = p.N;
+    f.H = p.H;
+    f.D = p.delta;
+    f.S = p.S;
+    f.key_side = 0;
+    f.causal = p.causal;
+    f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
+    RP_HIP(launch_finalize(dt, f, p.BH, s));
+  }
+  if (p.need_qside) {
+    PartialArgs pa;
+    pa.dz = dz;
+    pa.dz_bh = a.dz_bh;
+    pa.gi = at_off<GroupInfo>(ws, p.ws_gq);
+    pa.bnd = bndq;
+    pa.x = in->q;
+    pa.p1 = p.aq ? p1 : nullptr;
+    pa.p2 = (p.bias || p.v) ? p2 : nullptr;
+    pa.B = p.B;
+    pa.N = p.N;
+    pa.H = p.H;
+    pa.D = p.delta;
+    pa.S = p.S;
+    pa.nchunk = p.nchunk;
+    pa.key_side = 0;
+    pa.causal = p.causal;
+    RP_HIP(launch_partials(dt, pa, s));
+    if (p.aq) {
+      FoldArgs fa;
+      fa.p1 = p1;
+      fa.p2 = p2;
+      fa.fold = fold_ptr(p, ws, 0);
+      fa.vb = p.v ? in->vbias : nullptr;
+      fa.out = gr->daq;
+      fa.row_stride = desc->aq_row_stride;
+      fa.head_stride = desc->aq_head_stride;
+      fa.H = p.H;
+      fa.Ht = p.Htq;
+      fa.R = p.R;
+      fa.S = p.S;
+      fa.nchunk = p.nchunk;
+      fa.shared = p.aq_shared;
+      RP_HIP(launch_fold_table(dt, fa, s));
+    }
+    if (p.bias) {
+      FoldBiasArgs fb;
+      fb.p2 = p2;
+      fb.fold = fold_ptr(p, ws, 2);
+      fb.out = gr->dbias;
+      fb.row_stride = desc->bias_row_stride;
+      fb.head_stride = desc->bias_head_stride;
+      fb.H = p.H;
+      fb.R = p.R;
+      fb.S = p.S;
+      fb.nchunk = p.nchunk;
+      RP_HIP(launch_fold_bias(fb, s));
+    }
+    if (p.v) {
+      DvArgs dv;
+      dv.p2 = p2;
+      dv.atq = at_off<char>(ws, p.ws_atq);
+      dv.at_shared = p.aq_shared;
+      dv.out = gr->dvbias;
+      dv.H = p.H;
+      dv.S = p.S;
+      dv.nchunk = p.nchunk;
+      RP_HIP(launch_dv(dt, dv, s));
+    }
+  }
+
+  // Key-parallel pass, then the key reduction
+  RP_HIP(launch_attn_bwd_k(dt, bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0), a, p.B, s));
+  {
+    FinalizeArgs f;
+    std::memset(&f, 0, sizeof f);
+    f.acc = dkacc;
+    f.dz = p.ak ? dz : nullptr;
+    f.dz_bh = a.dz_bh;
+    f.gi = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+    f.bnd = p.ak ? bndk : nullptr;
+    f.at = p.ak ? at_off<char>(ws, p.ws_atk) : nullptr;
+    f.at_shared = p.ak_shared;
+    f.colsum = p.u ? colsum : nullptr;
+    f.u = p.u ? in->u : nullptr;
+    f.out = gr->dk;
+    f.N = p.N;
+    f.H = p.H;
+    f.D = p.delta;
+    f.S = p.S;
+    f.key_side = 1;
+    f.causal = p.causal;
+    f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
+    RP_HIP(launch_finalize(dt, f, p.BH, s));
+  }
+  if (p.ak) {
+    PartialArgs pa;
+    pa.dz = dz;
+    pa.dz_bh = a.dz_bh;
+    pa.gi = at_off<GroupInfo>(ws, p.ws_gk);
+    pa.bnd = bndk;
+    pa.x = in->k;
+    pa.p1 = p1;
+    pa.p2 = nullptr;
+    pa.B = p.B;
+    pa.N = p.N;
+    pa.H = p.H;
+    pa.D = p.delta;
+    pa.S = p.S;
+    pa.nchunk = p.nchunk;
+    pa.key_side = 1;
+    pa.causal = p.causal;
+    RP_HIP(launch_partials(dt, pa, s));
+    FoldArgs fa;
+    fa.p1 = p1;
+    fa.p2 = nullptr;
+    fa.fold = fold_ptr(p, ws, 1);
+    fa.vb = nullptr;
+    fa.out = gr->dak;
+    fa.row_stride = desc->ak_row_stride;
+    fa.head_stride = desc->ak_head_stride;
+    fa.H = p.H;
+    fa.Ht = p.Htk;
+    fa.R = p.R;
+    fa.S = p.S;
+    fa.nchunk = p.nchunk;
+    fa.shared = p.ak_shared;
+    RP_HIP(launch_fold_table(dt, fa, s));
+  }
+  if (p.u) {
+    DuArgs du;
+    du.colsum = colsum;
+    du.k = in->k;
+    du.out = gr->du;
+    du.B = p.B;
+    du.H = p.H;
+    du.N = p.N;
+    RP_HIP(launch_du(dt, du, s));
+  }
+  return RELPOS_OK;
+}
+
+}  // namespace
+}  // namespace relpos
+
+using namespace relpos;
+
+extern "C" {
+
+int relpos_plan_sizes(const relpos_desc* desc, const relpos_shape* shape, relpos_sizes* out) {
+  try {
+    if (out == nullptr) return fail(RELPOS_E_INVALID_ARG, "null output");
+    Plan p;
+    std::string detail;
+    int rc = make_plan(desc, shape, p, detail);
+    if (rc != RELPOS_OK) return fail(rc, detail);
+    out->z_bytes = p.z_bytes;
+    out->fwd_ws_bytes = p.ws_fwd_end;
+    out->fwd_ws_bytes_noz = p.ws_fwd_end + p.z_bytes;
+    out->bwd_ws_bytes = p.ws_bwd_end;
+    out->bwd_ws_bytes_noz = p.ws_bwd_end + p.z_bytes;
+    out->delta = p.delta;
+    out->expanded_rows = p.S;
+    out->group_size = kGroup;
+    out->num_groups = p.NG;
+    return RELPOS_OK;
+  } catch (const std::exception& e) {
+    return fail(RELPOS_E_INVALID_ARG, e.what());
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "unknown host error");
+  }
+}
+
+int relpos_plan_rows(const relpos_desc* desc, const relpos_shape* shape, int32_t which,
+                     int32_t* rows_out, int32_t cap) {
+  try {
+    Plan p;
+    std::string detail;
+    int rc = make_plan(desc, shape, p, detail);
+    if (rc != RELPOS_OK) return fail(rc, detail);
+    const std::vector<int32_t>* b = which == 0 ? &p.beta_q : which == 1 ? &p.beta_k
+                                     : which == 2 ? &p.beta_b : nullptr;
+    if (b == nullptr || rows_out == nullptr) return fail(RELPOS_E_INVALID_ARG, "bad table index");
+    if (cap < p.S) return fail(RELPOS_E_INVALID_ARG, "capacity too small");
+    for (int s = 0; s < p.S; ++s) rows_out[s] = (*b)[s];
+    return p.S;
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "host error");
+  }
+}
+
+int relpos_project(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+                   void* z, size_t z_bytes, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return run_project(desc, shape, in, z, z_bytes, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "host error");
+  }
+}
+
+int relpos_attn_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+                    const void* z, size_t z_bytes, void* o, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  try {
+    return run_fwd(desc, shape, in, z, z_bytes, o, lse, ws, ws_bytes,
+                   static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "host error");
+  }
+}
+
+int relpos_attn_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
+                    const void* z, size_t z_bytes, const void* o, const float* lse,
+                    const void* dout, relpos_grads* grads, void* ws, size_t ws_bytes,
+                    void* stream) {
+  try {
+    return run_bwd(desc, shape, in, z, z_bytes, o, lse, dout, grads, ws, ws_bytes,
+                   static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "host error");
+  }
+}
+
+const char* relpos_strerror(int code) {
+  switch (code) {
+    case RELPOS_OK:
+      return "success";
+    case RELPOS_E_INVALID_ARG:
+      return "invalid argument";
+    case RELPOS_E_UNSUPPORTED:
+      return "unsupported configuration";
+    case RELPOS_E_UNSUPPORTED_MAP:
+      return "unsupported relation map";
+    case RELPOS_E_MISALIGNED:
+      return "misaligned pointer or stride";
+    case RELPOS_E_WORKSPACE_TOO_SMALL:
+      return "buffer too small";
+    case RELPOS_E_HIP:
+      return "HIP error";
+    case RELPOS_E_ABI:
+      return "ABI version mismatch";
+    default:
+      return "unknown error";
+  }
+}
+
+const char* relpos_last_error(void) { return g_last_error.c_str(); }
+
+int relpos_abi_version(void) { return RELPOS_ABI_VERSION; }
+
+}  // extern "C"

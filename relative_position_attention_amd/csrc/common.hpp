@@ -1,0 +1,159 @@
+// Device helpers shared by the gfx950 kernels: element types, MFMA fragments,
+// small vector loads/stores, wave reductions.
+//
+// MFMA usage.  Every product uses the 16x16 output tile of
+// v_mfma_f32_16x16x32_bf16 (bf16 inputs) or v_mfma_f32_16x16x4_f32 (fp32
+// inputs).  Both share the output layout: lane l holds rows 4*(l>>4)+t,
+// t = 0..3, of column l&15.  Lane l supplies, for A, row l&15 and for B,
+// column l&15, with E consecutive K-elements starting at E*(l>>4) (E = 8 for
+// bf16, 1 for fp32); one MFMA covers K = 4E.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace relpos {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int E = 8;
+  static constexpr int KS = 32;
+  using frag = bf16x8;
+  static __device__ __forceinline__ floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (bf16)0.f;
+    return f;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int E = 1;
+  static constexpr int KS = 4;
+  using frag = float;
+  static __device__ __forceinline__ floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ frag zero() { return 0.f; }
+};
+
+// Storage type of the projections Z (fp16 for bf16 inputs, [RPA] "Half-
+// precision numerics") and of the offset gradients (input precision).
+template <typename T>
+struct Store;
+template <>
+struct Store<bf16> {
+  using Z = _Float16;
+  using G = bf16;
+};
+template <>
+struct Store<float> {
+  using Z = float;
+  using G = float;
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ float to_f(_Float16 x) { return static_cast<float>(x); }
+
+template <typename T>
+__device__ __forceinline__ T from_f(float x);
+template <>
+__device__ __forceinline__ float from_f<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ bf16 from_f<bf16>(float x) {
+  return static_cast<bf16>(x);
+}
+template <>
+__device__ __forceinline__ _Float16 from_f<_Float16>(float x) {
+  // clamp to the fp16 range so an outlier cannot overflow to infinity
+  x = fminf(fmaxf(x, -65504.f), 65504.f);
+  return static_cast<_Float16>(x);
+}
+
+// 4 consecutive elements (aligned run) -> float[4]
+__device__ __forceinline__ void load4(const _Float16* p, float* out) {
+  halfx4 v = *reinterpret_cast<const halfx4*>(p);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) out[t] = static_cast<float>(v[t]);
+}
+__device__ __forceinline__ void load4(const float* p, float* out) {
+  floatx4 v = *reinterpret_cast<const floatx4*>(p);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) out[t] = v[t];
+}
+__device__ __forceinline__ void store4(bf16* p, const float* in) {
+  bf16x4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = static_cast<bf16>(in[t]);
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, const float* in) {
+  floatx4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = in[t];
+  *reinterpret_cast<floatx4*>(p) = v;
+}
+
+// Four consecutive fp32 values at p[idx..idx+3]; entries at or past `n` read 0.
+// One 16-byte load when in range and aligned, else scalar loads.
+__device__ __forceinline__ void load4_guard(const float* p, int idx, int n, float* out) {
+  if (idx + 3 < n && (reinterpret_cast<uintptr_t>(p + idx) & 15) == 0) {
+    floatx4 v = *reinterpret_cast<const floatx4*>(p + idx);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = v[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = (idx + t < n) ? p[idx + t] : 0.f;
+  }
+}
+
+__device__ __forceinline__ float wave_max_g(float v) {
+  // reduce over the four lane groups l>>4 that share l&15
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_g(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Output element store (O, dQ, dK, dV) in the output dtype.
+__device__ __forceinline__ void store_out4(void* base, int64_t idx, bool f32, const float* v) {
+  if (f32)
+    store4(reinterpret_cast<float*>(base) + idx, v);
+  else
+    store4(reinterpret_cast<bf16*>(base) + idx, v);
+}
+
+}  // namespace relpos

@@ -1,0 +1,225 @@
+// Kernel argument blocks and host-side launch entry points.
+// [RPA] = "Fast and Exact Relative-Position Attention via Structure-Aware
+// Kernels" (arXiv 2611.01182).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.hpp"
+
+namespace relpos {
+
+// Template flags of the attention kernels (compile-time specialisation per
+// active term, map class and mask, [RPA] §4.3.3).
+enum : int {
+  F_ZQ = 1,      // read the query projections Z^Q (A^Q, with b and v folded in)
+  F_ZK = 2,      // read the key projections Z^K
+  F_BT = 4,      // read the expanded bias table directly (no Z^Q)
+  F_CAUSAL = 8,  // j > i masked
+  F_DZQ = 16,    // backward: query-side offset gradients (A^Q, b or v present)
+  F_DZK = 32,    // backward: key-side offset gradients (A^K present)
+  F_U = 64,      // backward: key column sums of G (Transformer-XL u term)
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const void* zq;  // projection slices (Z element type)
+  const void* zk;
+  int64_t zq_bh, zk_bh;  // elements per (b, h) slice
+  const GroupInfo* gq;
+  const GroupInfo* gk;
+  const float* rowlo;
+  const float* rowhi;
+  const float* keylo;
+  const float* keyhi;
+  const float* keymid;
+  const float* bt;  // [H, S] expanded bias (b and v folded), fp32
+  void* o;          // forward output / backward input (out dtype)
+  float* lse;       // natural-log logsumexp
+  const float* dvec;  // backward: D = rowdot(dO, O)
+  float* dqacc;       // backward: tau dS K, fp32 [BH, N, 64]
+  float* dkacc;       // backward: tau dS^T Q, fp32
+  void* dv;           // backward: dV (out dtype)
+  void* dz;           // backward: offset gradients (input precision)
+  int64_t dz_bh;
+  float* bndq;    // [BH, N, 2] boundary sums (rows 0 and 2D) of the queries
+  float* bndk;    // [BH, N, 2] of the keys
+  float* colsum;  // [BH, N] sum_i G_ij
+  int N, H, D, S;
+  float scale;       // tau
+  float scale_log2;  // tau * log2(e)
+  int out_f32;
+};
+
+// dtype: 0 = fp32 inputs, 1 = bf16 inputs.  Return hipError_t of the launch.
+hipError_t launch_attn_fwd(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_bwd_q(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_bwd_k(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+
+// ---- auxiliary kernels (aux.hip)
+
+// Plan metadata built on the device (no host-to-device copies).
+struct MetaArgs {
+  GroupInfo* gq;  // may be null
+  GroupInfo* gk;  // may be null
+  int N, NG, D;
+  int causal;
+};
+hipError_t launch_meta_groups(const MetaArgs& m, hipStream_t s);
+
+// A small block of host-built int32 metadata, passed by value and written to
+// device memory by one launch (kernel-argument upload, fully asynchronous).
+constexpr int kMetaChunk = 896;
+struct MetaChunk {
+  int32_t* dst;
+  int count;
+  int32_t vals[kMetaChunk];
+};
+hipError_t launch_meta_fill(const MetaChunk& c, hipStream_t s);
+
+// Affine maps (identity / clipped): beta and fold intervals on the device.
+struct AffineMapArgs {
+  int32_t* beta;      // [S]
+  int kind;           // RELPOS_MAP_IDENTITY or RELPOS_MAP_CLIPPED
+  int sign, offset, clip;
+  int D, S, R, causal;
+};
+hipError_t launch_meta_affine(const AffineMapArgs& m, hipStream_t s);
+
+// fold[r] = first and last expanded row s with beta(s) = r ([1, 0] if none)
+hipError_t launch_fold_meta(const int32_t* beta, int32_t* fold, int S, int R, hipStream_t s);
+
+struct ExpandArgs {
+  const void* table;  // original table (input dtype)
+  int64_t row_stride, head_stride;
+  const int32_t* beta;
+  void* out;  // [Ht, S, 64] input dtype
+  int Ht, S;
+};
+hipError_t launch_expand(int dtype, const ExpandArgs& e, hipStream_t s);
+
+struct BiasExpandArgs {
+  const void* bias;  // [R, H] with strides (input dtype), may be null
+  int64_t row_stride, head_stride;
+  const int32_t* beta_b;
+  const void* vb;    // [H, 64] v bias (input dtype), may be null
+  const void* atq;   // expanded A^Q [Htq, S, 64], needed with vb
+  int htq_shared;
+  float* bt;         // [H, S]
+  int H, S;
+};
+hipError_t launch_bias_expand(int dtype, const BiasExpandArgs& e, hipStream_t s);
+
+struct ProjectArgs {
+  const void* x;       // queries or keys [BH, N, 64]
+  const void* at;      // expanded table [Ht, S, 64]
+  int at_shared;
+  const float* bt;     // [H, S] added to every entry (query side), or null
+  const GroupInfo* gi;
+  void* z;             // Z slices
+  int64_t z_bh;
+  int N, H, D, S, NG;
+};
+hipError_t launch_project(int dtype, const ProjectArgs& p, int BH, int max_pitch, hipStream_t s);
+
+struct RowKeyArgs {
+  const void* q;
+  const void* k;
+  const void* atq;  // [Htq, S, 64] or null
+  const void* atk;  // [Htk, S, 64] or null
+  int atq_shared, atk_shared;
+  const float* bt;  // [H, S]
+  const void* u;    // [H, 64] or null
+  float* rowlo;
+  float* rowhi;
+  float* keylo;
+  float* keyhi;
+  float* keymid;
+  int N, H, S;
+};
+hipError_t launch_rowkey(int dtype, const RowKeyArgs& a, int BH, hipStream_t s);
+
+hipError_t launch_rowdot(int dtype, int out_f32, const void* o, const void* dout, float* dvec,
+                         int64_t rows, hipStream_t s);
+
+// Completion of dQ (query side) or dK (key side):
+//   out = acc + sum_s dZ~[i, s] A~[s] (band rows, MFMA) + boundary rows in fp32
+//         (+ colsum * u on the key side).
+struct FinalizeArgs {
+  const float* acc;  // [BH, N, 64]
+  const void* dz;    // offset gradients, null if the side has no table
+  int64_t dz_bh;
+  const GroupInfo* gi;
+  const float* bnd;  // [BH, N, 2]
+  const void* at;    // expanded table [Ht, S, 64] (input dtype), null if none
+  int at_shared;
+  const float* colsum;  // key side with u, else null
+  const void* u;        // [H, 64]
+  void* out;            // out dtype
+  int N, H, D, S, key_side, causal, out_f32;
+};
+hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s);
+
+// Table-gradient partials per (head, token chunk) ([RPA] "Deterministic table
+// gradients", first kernel): P1[h][c][s][:] = sum_i dZ~[i,s] x_i,
+// P2[h][c][s] = sum_i dZ~[i,s].
+struct PartialArgs {
+  const void* dz;
+  int64_t dz_bh;
+  const GroupInfo* gi;
+  const float* bnd;
+  const void* x;  // q or k [BH, N, 64] (input dtype)
+  float* p1;      // [H, nchunk, S, 64] or null
+  float* p2;      // [H, nchunk, S] or null
+  int B, N, H, D, S, nchunk, key_side, causal;
+};
+hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s);
+
+// Second kernel: fixed-order sums over chunks (and heads of a shared table),
+// then the bucket fold dA[r] = sum over copies s of r ([RPA] App. B.1
+// bucket-copy lemma), written with the table's strides.
+struct FoldArgs {
+  const float* p1;
+  const float* p2;
+  const int32_t* fold;  // [R, 2] intervals
+  const void* vb;       // v bias [H, 64] (query side with V), else null
+  float* out;
+  int64_t row_stride, head_stride;
+  int H, Ht, R, S, nchunk, shared;
+};
+hipError_t launch_fold_table(int dtype, const FoldArgs& f, hipStream_t s);
+
+struct FoldBiasArgs {
+  const float* p2;
+  const int32_t* fold;
+  float* out;
+  int64_t row_stride, head_stride;
+  int H, R, S, nchunk;
+};
+hipError_t launch_fold_bias(const FoldBiasArgs& f, hipStream_t s);
+
+// dv[h] = sum_s (sum_c P2[h][c][s]) A~^Q[s]
+struct DvArgs {
+  const float* p2;
+  const void* atq;
+  int at_shared;
+  float* out;
+  int H, S, nchunk;
+};
+hipError_t launch_dv(int dtype, const DvArgs& a, hipStream_t s);
+
+// du[h] = sum_{b,j} colsum[b,h,j] k[b,h,j]
+struct DuArgs {
+  const float* colsum;
+  const void* k;
+  float* out;
+  int B, H, N;
+};
+hipError_t launch_du(int dtype, const DuArgs& a, hipStream_t s);
+
+}  // namespace relpos

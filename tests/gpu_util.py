@@ -1,0 +1,55 @@
+"""Helpers of the GPU parity tests: device transfer, library calls, the
+tolerance check."""
+
+import numpy as np
+import torch
+
+import relative_position_attention_amd as rpa
+
+# Tolerances of the parity contract (per tensor, against the fp64 oracle).
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-2)}  # (max-abs, relative L2)
+
+GRAD_KEYS = ("dq", "dk", "dv", "daq", "dak", "dbias", "du", "dv_bias")
+
+
+def to_device(spec, arrays):
+    dt = torch.float32 if spec["dtype"] == "f32" else torch.bfloat16
+    out = {}
+    for name, arr in arrays.items():
+        # values are exactly representable in dt: the conversion is exact
+        out[name] = torch.from_numpy(np.ascontiguousarray(arr)).to(dt).cuda()
+    return out
+
+
+def run_library(spec, arrays, out_dtype="f32", retain=True):
+    prob = rpa.Problem(spec, out_dtype=out_dtype)
+    t = to_device(spec, arrays)
+    o, lse, z = rpa.attn_fwd(prob, t, retain=retain)
+    grads = rpa.attn_bwd(prob, t, o, lse, t["do"], z=z)
+    torch.cuda.synchronize()
+    res = {"o": o, "lse": lse}
+    res.update(grads)
+    return {k: v.double().cpu().numpy() for k, v in res.items()}
+
+
+def errors(got, ref):
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff) / den) if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def check(spec, got, ref, keys=None, label="", report=None):
+    tol_abs, tol_rel = TOL[spec["dtype"]]
+    keys = keys or [k for k in ("o",) + GRAD_KEYS if k in ref]
+    failures = []
+    for key in keys:
+        ma, rl = errors(got[key], ref[key])
+        line = f"{label} {key:8s} max_abs={ma:.3e} rel_l2={rl:.3e}"
+        print(line, flush=True)
+        if report is not None:
+            report.append(line)
+        if not (ma <= tol_abs and rl <= tol_rel):
+            failures.append(line)
+    assert not failures, "\n".join(failures)
