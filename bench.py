@@ -1,0 +1,265 @@
+"""Benchmark: forward / backward of exact relative-position attention at 8K
+tokens for the four mechanisms, on one MI355X.
+
+One step = for each mechanism (Shaw clipped 256, T5 buckets, DeBERTa c2p+p2c,
+Transformer-XL causal) at its 8192-token shape: relpos_project +
+relpos_attn_fwd (the forward) and relpos_attn_bwd (the backward, retained
+projections), inputs resident in HBM.  Prints one JSON line.
+
+Useful FLOPs follow the credit of "Fast and Exact Relative-Position Attention
+via Structure-Aware Kernels" (§5.1 evaluation setup, throughput paragraph):
+forward 4 B H N^2 d + 2 B H N R d per projected table (none for T5), backward
+twice the forward; the attention part of a causal problem is credited for the
+visible pairs only.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mechs shaw,t5,...]
+                    [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk
+MI355X_HBM_GBPS = 8000.0
+MECHS = ("shaw", "t5", "deberta", "txl")
+
+
+def credited_flops(spec):
+    """(forward, backward) useful FLOPs of one problem."""
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    attn = 4.0 * B * H * N * N * d
+    if spec["causal"]:
+        attn *= (N + 1) / (2.0 * N)
+    nproj = sum(1 for t in ("aq", "ak") if t in spec["terms"])
+    R = spec.get("rows", 0)
+    fwd = attn + nproj * 2.0 * B * H * N * R * d
+    return fwd, 2.0 * fwd
+
+
+def attention_flops(spec):
+    """MFMA FLOPs of the forward attention kernel alone (QK^T and PV)."""
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    attn = 4.0 * B * H * N * N * d
+    if spec["causal"]:
+        attn *= (N + 1) / (2.0 * N)
+    return attn
+
+
+class MechRun:
+    """Device inputs and preallocated outputs of one mechanism."""
+
+    def __init__(self, name, torch, rpa, synth):
+        self.name = name
+        spec, arr = synth.make_bench(name)
+        self.spec = spec
+        dt = torch.bfloat16
+        self.t = {k: torch.from_numpy(v).to(dt).cuda() for k, v in arr.items()}
+        del arr
+        # outputs in fp32: the configuration the parity tests check
+        self.prob = rpa.Problem(spec, out_dtype="f32")
+        sz = rpa.plan_sizes(self.prob)
+        self.sizes = sz
+        dev = self.t["q"].device
+        B, H, N = spec["B"], spec["H"], spec["N"]
+        self.z = torch.empty(max(sz["z_bytes"], 256), dtype=torch.uint8, device=dev)
+        self.ws_f = torch.empty(max(sz["fwd_ws_bytes"], 256), dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty(max(sz["bwd_ws_bytes"], 256), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((B, H, N, 64), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        self.grads = rpa.empty_grads(self.prob, dev)
+        self.fwd_flops, self.bwd_flops = credited_flops(spec)
+        self.attn_flops = attention_flops(spec)
+
+    def project(self, rpa):
+        rpa.project(self.prob, self.t, z=self.z, ws=self.ws_f)
+
+    def attn(self, rpa):
+        rpa.attn_fwd(self.prob, self.t, z=self.z, o=self.o, lse=self.lse)
+
+    def backward(self, rpa):
+        rpa.attn_bwd(self.prob, self.t, self.o, self.lse, self.t["do"], z=self.z,
+                     grads=self.grads, ws=self.ws_b)
+
+
+def peak_memory(run, torch, rpa):
+    """Peak device MiB beyond the inputs of a forward and of a backward that
+    allocate their own buffers (the library itself never allocates)."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, lse, z = rpa.attn_fwd(run.prob, run.t, retain=True)
+    torch.cuda.synchronize()
+    fwd = (torch.cuda.max_memory_allocated() - base) / 2**20
+    base2 = torch.cuda.memory_allocated()  # inputs + O + L + retained z
+    base2 -= z.numel()  # the retained projections count against the backward
+    torch.cuda.reset_peak_memory_stats()
+    g = rpa.attn_bwd(run.prob, run.t, o, lse, run.t["do"], z=z)
+    torch.cuda.synchronize()
+    bwd = (torch.cuda.max_memory_allocated() - base2) / 2**20
+    del o, lse, z, g
+    torch.cuda.empty_cache()
+    return fwd, bwd
+
+
+def cpu_baseline(mechs):
+    """The fp64 oracle on one (batch, head) slice of each mechanism's bench
+    shape, timed on the host; credited FLOPs of those slices per second."""
+    import numpy as np  # noqa: F401
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    total_s, total_flops = 0.0, 0.0
+    for name in mechs:
+        kw = dict(synth.BENCH_SHAPES[name])
+        B, H = kw["B"], kw["H"]
+        spec, arr = synth.make_problem(**dict(kw, B=1, H=1))
+        t0 = time.perf_counter()
+        oracle.slice_forward_backward(spec, arr, 0, 0)
+        total_s += time.perf_counter() - t0
+        f, b = credited_flops(spec)
+        total_flops += f + b
+        del arr
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one (batch, head) slice of each of {','.join(mechs)} at N=8192, "
+                      f"fp64 forward+backward ({total_s:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--mechs", default=",".join(MECHS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-memory", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this library has no "
+              "multi-GPU path; heads and batch shard with no communication, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import relative_position_attention_amd as rpa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rpa.library()  # fails loudly if the HIP library is missing
+    mechs = [m for m in args.mechs.split(",") if m]
+    runs = [MechRun(m, torch, rpa, synth) for m in mechs]
+    stream = torch.cuda.current_stream()
+
+    mem = {}
+    if not args.no_memory:
+        for r in runs:
+            mem[r.name] = peak_memory(r, torch, rpa)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    for _ in range(args.warmup):
+        for r in runs:
+            r.project(rpa)
+            r.attn(rpa)
+            r.backward(rpa)
+    torch.cuda.synchronize()
+
+    marks = []
+    torch.cuda.synchronize()
+    t_start = ev()
+    for _ in range(args.steps):
+        row = []
+        for r in runs:
+            e0 = ev()
+            r.project(rpa)
+            e1 = ev()
+            r.attn(rpa)
+            e2 = ev()
+            r.backward(rpa)
+            e3 = ev()
+            row.append((e0, e1, e2, e3))
+        marks.append(row)
+    t_end = ev()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per = {}
+    step_flops = 0.0
+    for k, r in enumerate(runs):
+        proj = sum(m[k][0].elapsed_time(m[k][1]) for m in marks) / args.steps
+        attn = sum(m[k][1].elapsed_time(m[k][2]) for m in marks) / args.steps
+        bwd = sum(m[k][2].elapsed_time(m[k][3]) for m in marks) / args.steps
+        fwd = proj + attn
+        step_flops += r.fwd_flops + r.bwd_flops
+        d = {
+            "shape": {x: r.spec[x] for x in ("B", "H", "N", "causal")},
+            "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+            "project_ms": round(proj, 4), "attn_kernel_ms": round(attn, 4),
+            "fwd_tflops": round(r.fwd_flops / fwd / 1e9, 2),
+            "bwd_tflops": round(r.bwd_flops / bwd / 1e9, 2),
+            "fwd_pct_peak": round(100 * r.fwd_flops / fwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * r.bwd_flops / bwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
+            "attn_kernel_tflops": round(r.attn_flops / attn / 1e9, 2),
+        }
+        if r.name in mem:
+            d["fwd_peak_mib"] = round(mem[r.name][0], 1)
+            d["bwd_peak_mib"] = round(mem[r.name][1], 1)
+        per[r.name] = d
+
+    # Dominant single-launch kernel timed live: the forward attention kernel
+    # (relpos_attn_fwd with retained projections is exactly one launch).
+    dom = max(runs, key=lambda r: per[r.name]["attn_kernel_ms"])
+    dom_ms = per[dom.name]["attn_kernel_ms"]
+    achieved = dom.attn_flops / dom_ms / 1e9
+    roofline = {"bound": "mfma", "kernel": f"attn_fwd_kernel ({dom.name})",
+                "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
+                "traffic": None}
+
+    value = step_flops / ms_per_step / 1e9
+    out = {
+        "metric": "fwd/bwd ms + TFLOP/s (% bf16 MFMA peak) per mechanism at N=8K; peak MiB",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "relpos attention fwd+bwd at N=8192: " + ", ".join(
+            f"{r.name} B{r.spec['B']} H{r.spec['H']}{' causal' if r.spec['causal'] else ''}"
+            for r in runs), "mechanisms": mechs, "d": 64},
+        "mechanisms": per,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        del runs
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(mechs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

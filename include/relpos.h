@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 1
+#define RELPOS_ABI_VERSION 2
 
 /* ---- return codes ---------------------------------------------------- */
 #define RELPOS_OK 0
@@ -95,6 +95,14 @@ typedef struct relpos_desc {
   int32_t out_dtype;       /* O, dQ, dK, dV                                  */
   int32_t num_rows;        /* R: rows of every relation table                */
   int32_t sign_q, sign_k, sign_b; /* +1 or -1 (see conventions)              */
+  /* Precision of the probability and score-gradient operands of the MFMA
+     products O = P V, dV = P^T dO, dQ = G K and dK = G^T Q (G = tau dS;
+     bf16 inputs only, ignored for fp32): 0 = rounded once to bf16 (8
+     significant bits, [RPA] "Half-precision numerics"); 1 = a bf16 pair
+     hi + lo (about 16 significant bits; one more MFMA product each), for a
+     strongly peaked softmax such as tau = 1 with unit-variance inputs, where
+     an 8-bit P moves O, hence D = rowdot(dO, O), by more than 2^-9. */
+  int32_t split_operands;
   relpos_map map;
   /* Table layouts, in elements.  A^Q, A^K: element (r, h, e) at
      r*row_stride + h*head_stride + e (e < 64 contiguous).  head_stride 0
@@ -127,7 +135,8 @@ typedef struct relpos_grads {
 
 typedef struct relpos_sizes {
   size_t z_bytes;          /* retained projection buffer                     */
-  size_t fwd_ws_bytes;     /* relpos_attn_fwd / relpos_project workspace     */
+  size_t fwd_ws_bytes;     /* relpos_project workspace (relpos_attn_fwd with
+                              retained z needs none: ws may be NULL)         */
   size_t fwd_ws_bytes_noz; /* relpos_attn_fwd workspace when z == NULL       */
   size_t bwd_ws_bytes;     /* relpos_attn_bwd workspace                      */
   size_t bwd_ws_bytes_noz; /* relpos_attn_bwd workspace when z == NULL       */
@@ -160,7 +169,7 @@ int relpos_plan_rows(const relpos_desc *desc, const relpos_shape *shape,
                      int32_t which, int32_t *rows_out, int32_t cap);
 
 /*
- * relpos_project -- [RPA] Table 9 "Projection" (Algorithm 1, lines 1-4):
+ * relpos_project -- [RPA] Table 9 "Projection" (the projection step of Algorithm 1):
  * bucket copies of the tables, then Z^Q = Q (A^Q over each group's reachable
  * rows)^T (+ b folded in, [RPA] "Kernel structure") and Z^K likewise, stored
  * fp16 (fp32 for fp32 inputs) in `z`, plus per-token boundary entries.
@@ -171,7 +180,7 @@ int relpos_project(const relpos_desc *desc, const relpos_shape *shape,
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
- * relpos_attn_fwd -- [RPA] Table 9 "Attention" (Algorithm 1, lines 5-21):
+ * relpos_attn_fwd -- [RPA] Table 9 "Attention" (the tiled loop of Algorithm 1):
  * the tiled online-softmax forward with offset-aware tiles (three key ranges
  * per query tile: saturated-high, band, saturated-low).  Writes
  * O [B,H,N,64] (out_dtype) and L [B,H,N] fp32, L_i = ln sum_j exp(S_ij).

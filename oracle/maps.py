@@ -2,10 +2,10 @@
 
 [RPA] lists three map families: identity (row = offset + N - 1), clipped
 (row = clip(offset, -D, D) + D) and bucketed (offsets split into consecutive
-ordered buckets).  The two bucketed maps of the evaluated mechanisms are
-named in [RPA] §5.1 "Mechanisms" -- "32 bidirectional buckets up to distance
-128, as in the original T5" and "256 logarithmic buckets up to distance 512,
-as in DeBERTa-v3" -- without formulas.  They are written here from their
+ordered buckets).  [RPA] §5.1 "Mechanisms" names the two bucketed maps of the
+evaluated mechanisms only by their origin (T5's 32 bidirectional buckets with
+maximum distance 128; DeBERTa-v3's 256 logarithmic buckets with maximum
+position 512) and prints no formula.  They are written here from their
 standard definitions, evaluated EXACTLY with integer arithmetic (no floating
 logarithm), so that no rounding decides a bucket boundary.
 

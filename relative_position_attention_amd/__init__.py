@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     project,
     attn_fwd,
     attn_bwd,
+    empty_grads,
     strerror,
     EXPORTED_SYMBOLS,
 )

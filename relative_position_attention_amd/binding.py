@@ -11,7 +11,7 @@ EXPORTED_SYMBOLS = (
     "relpos_attn_bwd", "relpos_strerror", "relpos_last_error", "relpos_abi_version",
 )
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAP_KIND = {"identity": 0, "clipped": 1, "t5": 2, "log": 3, "explicit": 4}
 DTYPE = {"f32": 0, "bf16": 1}
 TERM = {"aq": 1, "ak": 2, "bias": 4, "u": 8, "v": 16}
@@ -36,7 +36,8 @@ class _Desc(ctypes.Structure):
                 ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("num_rows", ctypes.c_int32), ("sign_q", ctypes.c_int32),
-                ("sign_k", ctypes.c_int32), ("sign_b", ctypes.c_int32), ("map", _Map),
+                ("sign_k", ctypes.c_int32), ("sign_b", ctypes.c_int32),
+                ("split_operands", ctypes.c_int32), ("map", _Map),
                 ("aq_row_stride", ctypes.c_int64), ("aq_head_stride", ctypes.c_int64),
                 ("ak_row_stride", ctypes.c_int64), ("ak_head_stride", ctypes.c_int64),
                 ("bias_row_stride", ctypes.c_int64), ("bias_head_stride", ctypes.c_int64)]
@@ -141,6 +142,7 @@ class Problem:
         d.sign_q = int(signs.get("aq", 1))
         d.sign_k = int(signs.get("ak", 1))
         d.sign_b = int(signs.get("bias", 1))
+        d.split_operands = int(bool(spec.get("split_operands", False)))
         mp = spec["map"]
         d.map.kind = MAP_KIND[mp["kind"]]
         d.map.clip = int(mp.get("clip", 0))
@@ -256,12 +258,14 @@ def attn_fwd(problem, t, z=None, retain=True, o=None, lse=None, ws=None):
         o = torch.empty((B, H, N, 64), dtype=_out_torch_dtype(problem), device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = _empty_bytes(sz["fwd_ws_bytes"] if z is not None else sz["fwd_ws_bytes_noz"], dev)
+    if ws is None and z is None:
+        ws = _empty_bytes(sz["fwd_ws_bytes_noz"], dev)
+    # with retained projections the forward needs no workspace
     _check(library().relpos_attn_fwd(ctypes.byref(problem.desc), ctypes.byref(problem.shape),
                                      ctypes.byref(_tensors(problem, t)), _ptr(z),
                                      0 if z is None else z.numel(), _ptr(o), _ptr(lse),
-                                     _ptr(ws), ws.numel(), _stream()), "relpos_attn_fwd")
+                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+           "relpos_attn_fwd")
     return o, lse, z
 
 

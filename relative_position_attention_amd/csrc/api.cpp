@@ -72,16 +72,23 @@ int check_inputs(const Plan& p, const relpos_tensors* in) {
   return RELPOS_OK;
 }
 
-// Group tables, expanded row maps and fold intervals, built on the device.
-int build_meta(const Plan& p, void* ws, hipStream_t s) {
+// Group tables of the projection layout, built on the device into z (the
+// attention kernels read them from there, so a forward with retained z
+// launches nothing else).
+int build_groups(const Plan& p, void* z, hipStream_t s) {
   MetaArgs m;
-  m.gq = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
-  m.gk = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+  m.gq = p.need_qside ? at_off<GroupInfo>(z, p.z_gq) : nullptr;
+  m.gk = p.ak ? at_off<GroupInfo>(z, p.z_gk) : nullptr;
   m.N = p.N;
   m.NG = p.NG;
   m.D = p.delta;
   m.causal = p.causal;
   if (m.gq || m.gk) RP_HIP(launch_meta_groups(m, s));
+  return RELPOS_OK;
+}
+
+// Expanded row maps and fold intervals, built on the device into ws.
+int build_maps(const Plan& p, void* ws, hipStream_t s) {
   struct Tab {
     bool on;
     const std::vector<int32_t>* beta;
@@ -186,7 +193,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.at = at_off<char>(ws, p.ws_atq);
     pa.at_shared = p.aq_shared;
     pa.bt = zv.bt;
-    pa.gi = at_off<GroupInfo>(ws, p.ws_gq);
+    pa.gi = at_off<GroupInfo>(z, p.z_gq);
     pa.z = zv.zq;
     pa.z_bh = p.zq.bh_elems;
     pa.N = p.N;
@@ -202,7 +209,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.at = at_off<char>(ws, p.ws_atk);
     pa.at_shared = p.ak_shared;
     pa.bt = nullptr;
-    pa.gi = at_off<GroupInfo>(ws, p.ws_gk);
+    pa.gi = at_off<GroupInfo>(z, p.z_gk);
     pa.z = zv.zk;
     pa.z_bh = p.zk.bh_elems;
     pa.N = p.N;
@@ -244,8 +251,8 @@ AttnArgs attn_args(const Plan& p, const relpos_tensors* in, void* z, void* ws) {
   a.zk = zv.zk;
   a.zq_bh = p.aq ? p.zq.bh_elems : 0;
   a.zk_bh = p.ak ? p.zk.bh_elems : 0;
-  a.gq = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
-  a.gk = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+  a.gq = p.need_qside ? at_off<GroupInfo>(z, p.z_gq) : nullptr;
+  a.gk = p.ak ? at_off<GroupInfo>(z, p.z_gk) : nullptr;
   a.rowlo = zv.rowlo;
   a.rowhi = zv.rowhi;
   a.keylo = zv.keylo;
@@ -282,7 +289,8 @@ int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos
   if (ws == nullptr || ws_bytes < p.ws_fwd_end)
     return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
   if (!aligned16(z) || !aligned16(ws)) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
-  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
+  if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
   if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
   return project_into(p, desc, in, z, ws, s);
 }
@@ -298,20 +306,26 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (o == nullptr || lse == nullptr || !aligned16(o) || !aligned16(lse))
     return fail(o && lse ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG, "o / lse");
   void* z = const_cast<void*>(zc);
-  const size_t need = z ? p.ws_fwd_end : p.ws_fwd_end + p.z_bytes;
-  if (ws == nullptr || ws_bytes < need) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
+  // with retained projections the forward is the attention kernel alone and
+  // needs no workspace
+  const size_t need = z ? 0 : p.ws_fwd_end + p.z_bytes;
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
   if (z && z_bytes < p.z_bytes) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "z too small");
-  if (!aligned16(ws) || (z && !aligned16(z))) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
-  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if ((need > 0 && !aligned16(ws)) || (z && !aligned16(z)))
+    return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
   if (z == nullptr) {
     z = at_off<char>(ws, p.ws_fwd_end);
+    if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
+    if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
     if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
     if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   }
   AttnArgs a = attn_args(p, in, z, ws);
   a.o = o;
   a.lse = lse;
-  RP_HIP(launch_attn_fwd(p.dtype == RELPOS_DTYPE_F32 ? 0 : 1, base_flags(p), a, p.B, s));
+  RP_HIP(launch_attn_fwd(p.dtype == RELPOS_DTYPE_F32 ? 0 : 1,
+                         base_flags(p) | (p.split ? F_SPLIT : 0), a, p.B, s));
   return RELPOS_OK;
 }
 
@@ -338,10 +352,11 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (!aligned16(ws) || (z && !aligned16(z))) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
 
   const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
-  if ((rc = build_meta(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
   if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
   if (z == nullptr) {
     z = at_off<char>(ws, p.ws_bwd_end);
+    if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
     if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   }
   float* dvec = at_off<float>(ws, p.ws_D);
@@ -371,7 +386,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   a.bndq = bndq;
   a.bndk = bndk;
   a.colsum = colsum;
-  const int bf = base_flags(p);
+  const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
   RP_HIP(launch_attn_bwd_q(dt, bf | (p.need_qside ? F_DZQ : 0), a, p.B, s));
@@ -381,7 +396,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.acc = dqacc;
     f.dz = p.aq ? dz : nullptr;
     f.dz_bh = a.dz_bh;
-    f.gi = p.need_qside ? at_off<GroupInfo>(ws, p.ws_gq) : nullptr;
+    f.gi = p.need_qside ? at_off<GroupInfo>(z, p.z_gq) : nullptr;
     f.bnd = p.aq ? bndq : nullptr;
     f.at = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
     f.at_shared = p.aq_shared;
@@ -399,7 +414,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     PartialArgs pa;
     pa.dz = dz;
     pa.dz_bh = a.dz_bh;
-    pa.gi = at_off<GroupInfo>(ws, p.ws_gq);
+    pa.gi = at_off<GroupInfo>(z, p.z_gq);
     pa.bnd = bndq;
     pa.x = in->q;
     pa.p1 = p.aq ? p1 : nullptr;
@@ -412,6 +427,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.nchunk = p.nchunk;
     pa.key_side = 0;
     pa.causal = p.causal;
+    pa.dz_f32 = p.dzq_f32;
     RP_HIP(launch_partials(dt, pa, s));
     if (p.aq) {
       FoldArgs fa;
@@ -464,7 +480,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.acc = dkacc;
     f.dz = p.ak ? dz : nullptr;
     f.dz_bh = a.dz_bh;
-    f.gi = p.ak ? at_off<GroupInfo>(ws, p.ws_gk) : nullptr;
+    f.gi = p.ak ? at_off<GroupInfo>(z, p.z_gk) : nullptr;
     f.bnd = p.ak ? bndk : nullptr;
     f.at = p.ak ? at_off<char>(ws, p.ws_atk) : nullptr;
     f.at_shared = p.ak_shared;
@@ -484,7 +500,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     PartialArgs pa;
     pa.dz = dz;
     pa.dz_bh = a.dz_bh;
-    pa.gi = at_off<GroupInfo>(ws, p.ws_gk);
+    pa.gi = at_off<GroupInfo>(z, p.z_gk);
     pa.bnd = bndk;
     pa.x = in->k;
     pa.p1 = p1;
@@ -497,6 +513,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.nchunk = p.nchunk;
     pa.key_side = 1;
     pa.causal = p.causal;
+    pa.dz_f32 = 0;
     RP_HIP(launch_partials(dt, pa, s));
     FoldArgs fa;
     fa.p1 = p1;
@@ -542,7 +559,7 @@ int relpos_plan_sizes(const relpos_desc* desc, const relpos_shape* shape, relpos
     int rc = make_plan(desc, shape, p, detail);
     if (rc != RELPOS_OK) return fail(rc, detail);
     out->z_bytes = p.z_bytes;
-    out->fwd_ws_bytes = p.ws_fwd_end;
+    out->fwd_ws_bytes = p.ws_fwd_end;  // relpos_project; relpos_attn_fwd with z needs none
     out->fwd_ws_bytes_noz = p.ws_fwd_end + p.z_bytes;
     out->bwd_ws_bytes = p.ws_bwd_end;
     out->bwd_ws_bytes_noz = p.ws_bwd_end + p.z_bytes;

@@ -379,15 +379,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs f) {
 // the tokens of chunk c (fp32, written once per chunk; [RPA] "Deterministic
 // table gradients").  Band rows on MFMA from the input-precision entries;
 // the two boundary rows in fp32 from the boundary sums.
-template <typename T>
+template <typename T, typename GT>
 __global__ __launch_bounds__(256) void partials_kernel(PartialArgs p) {
   using M = Mma<T>;
   using Frag = typename M::frag;
-  using GT = typename Store<T>::G;
   constexpr int E = M::E, KS = M::KS, NST = 64 / KS;
   constexpr int P = TileP<T>::P;
-  __shared__ __attribute__((aligned(16))) T zt[64 * P];  // [s][token]
-  __shared__ __attribute__((aligned(16))) T xt[64 * P];  // [d][token]
+  constexpr int ZP = 68;  // fp32 row pitch: 16-byte rows, staggered banks
+  __shared__ __attribute__((aligned(16))) float zt[64 * ZP];  // [s][token]
+  __shared__ __attribute__((aligned(16))) T xt[64 * P];       // [d][token]
   __shared__ float bsh[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int s0 = blockIdx.x * 64;
@@ -447,16 +447,16 @@ __global__ __launch_bounds__(256) void partials_kernel(PartialArgs p) {
 #pragma unroll 4
       for (int e = 0; e < 16; ++e) {
         const int s = s0 + q4 + e;
-        T val = from_f<T>(0.f);
-        if (band_hit && i < p.N && s >= smin && s <= smax) val = row[s - gi.slo + gi.pad];
-        zt[(q4 + e) * P + tkn] = val;
+        float val = 0.f;
+        if (band_hit && i < p.N && s >= smin && s <= smax) val = to_f(row[s - gi.slo + gi.pad]);
+        zt[(q4 + e) * ZP + tkn] = val;
       }
     }
     __syncthreads();
     if (want_p1 && band_hit) {
 #pragma unroll
       for (int c = 0; c < NST; ++c) {
-        Frag a = M::load(zt + (16 * wave + c16) * P + c * KS + g * E);
+        Frag a = frag_f32<T>(zt + (16 * wave + c16) * ZP + c * KS + g * E);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           Frag bb = M::load(xt + (16 * db + c16) * P + c * KS + g * E);
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(256) void partials_kernel(PartialArgs p) {
     if (p.p2 != nullptr && band_hit) {
       const int s = tid >> 2, q = (tid & 3) * 16;
       float part = 0.f;
-      for (int e = 0; e < 16; ++e) part += to_f(zt[s * P + q + e]);
+      for (int e = 0; e < 16; ++e) part += zt[s * ZP + q + e];
       part += __shfl_xor(part, 1);
       part += __shfl_xor(part, 2);
       p2acc += part;
@@ -689,9 +689,11 @@ hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t
 hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s) {
   dim3 grid(nblk(p.S, 64), p.H, p.nchunk);
   if (dtype == 0)
-    hipLaunchKernelGGL(partials_kernel<float>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((partials_kernel<float, float>), grid, dim3(256), 0, s, p);
+  else if (p.dz_f32)
+    hipLaunchKernelGGL((partials_kernel<bf16, float>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(partials_kernel<bf16>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((partials_kernel<bf16, bf16>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -76,6 +76,19 @@ struct Store<float> {
   using G = float;
 };
 
+// Element type of the offset gradients dZ~ written by the backward passes:
+// the input precision ([RPA] "Half-precision numerics"), except fp32 for a
+// scalar bias without a query table, whose per-row sums cancel (every row of
+// dS sums to zero) and would lose the 8-bit entries' precision.
+template <typename T, bool BIAS_ONLY>
+struct DzType {
+  using type = typename Store<T>::G;
+};
+template <typename T>
+struct DzType<T, true> {
+  using type = float;
+};
+
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return static_cast<float>(x); }
 __device__ __forceinline__ float to_f(_Float16 x) { return static_cast<float>(x); }

@@ -21,6 +21,7 @@ enum : int {
   F_DZQ = 16,    // backward: query-side offset gradients (A^Q, b or v present)
   F_DZK = 32,    // backward: key-side offset gradients (A^K present)
   F_U = 64,      // backward: key column sums of G (Transformer-XL u term)
+  F_SPLIT = 128,  // bf16: P and G enter their MFMA products as bf16 hi + lo
 };
 
 struct AttnArgs {
@@ -177,6 +178,7 @@ struct PartialArgs {
   float* p1;      // [H, nchunk, S, 64] or null
   float* p2;      // [H, nchunk, S] or null
   int B, N, H, D, S, nchunk, key_side, causal;
+  int dz_f32;     // entries are fp32 (scalar bias without a query table)
 };
 hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s);
 

@@ -101,8 +101,9 @@ bool map_row(const relpos_map& mp, int64_t x, int64_t& row) {
       return true;
     }
     case RELPOS_MAP_T5_BUCKET: {
-      // T5 relative-position buckets ([RPA] §5.1 "Mechanisms": "as in the
-      // original T5"); x is T5's argument (key position minus query position).
+      // T5 relative-position buckets ([RPA] §5.1 "Mechanisms" names the
+      // original T5 scheme); x is T5's argument (key position minus query
+      // position).
       int64_t nb = mp.num_buckets;
       if (nb < 2 || mp.max_distance < 1) return false;
       int64_t ret = 0, n;
@@ -266,6 +267,10 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     detail = "out_dtype must be F32 or BF16";
     return RELPOS_E_INVALID_ARG;
   }
+  if (desc->split_operands != 0 && desc->split_operands != 1) {
+    detail = "split_operands must be 0 or 1";
+    return RELPOS_E_INVALID_ARG;
+  }
   if (!std::isfinite(desc->scale)) {
     detail = "scale must be finite";
     return RELPOS_E_INVALID_ARG;
@@ -288,6 +293,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.t_size = desc->dtype == RELPOS_DTYPE_F32 ? 4 : 2;
   p.z_size = p.t_size;  // fp16 projections for bf16 inputs ([RPA] "Half-precision numerics")
   p.g_size = p.t_size;  // offset gradients in the input precision
+  p.dzq_f32 = p.bias && !p.aq;  // ... except a bias alone: fp32 (sums cancel)
+  p.split = desc->split_operands != 0 && p.dtype == RELPOS_DTYPE_BF16;
   bool any_table = p.aq || p.ak || p.bias;
   if (any_table && p.R < 1) {
     detail = "num_rows must be >= 1";
@@ -401,8 +408,12 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   int want = (2048 + sblocks * p.H - 1) / std::max(1, sblocks * p.H);
   p.nchunk = std::max(1, std::min(want, subs));
 
-  // ---- z layout
+  // ---- z layout (group tables first)
   size_t off = 0;
+  p.z_gq = off;
+  off = align256(off + sizeof(GroupInfo) * p.NG);
+  p.z_gk = off;
+  off = align256(off + sizeof(GroupInfo) * p.NG);
   const size_t bhn4 = static_cast<size_t>(p.BH) * p.N * 4;
   if (p.aq) {
     p.z_zq = off;
@@ -428,10 +439,6 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
 
   // ---- workspace, forward part
   off = 0;
-  p.ws_gq = off;
-  off = align256(off + sizeof(GroupInfo) * p.NG);
-  p.ws_gk = off;
-  off = align256(off + sizeof(GroupInfo) * p.NG);
   p.ws_beta_q = off;
   off = align256(off + 4 * p.S);
   p.ws_beta_k = off;
@@ -457,11 +464,15 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   off = align256(off + bhn4 * kHeadDim);
   p.ws_dkacc = off;
   off = align256(off + bhn4 * kHeadDim);
+  // one buffer holds the query side's entries, then the key side's ([RPA]
+  // Table 9: the query reduction finishes before the key pass starts)
+  // (slice stride: the larger side's element count; entry size: the wider type)
   int64_t dz_elems = 0;
   if (p.need_qside) dz_elems = std::max(dz_elems, p.zq.bh_elems);
   if (p.ak) dz_elems = std::max(dz_elems, p.zk.bh_elems);
+  const size_t dz_entry = p.dzq_f32 ? 4 : p.g_size;
   p.ws_dz = off;
-  off = align256(off + static_cast<size_t>(p.BH) * dz_elems * p.g_size);
+  off = align256(off + static_cast<size_t>(p.BH) * dz_elems * dz_entry);
   p.ws_bndq = off;
   off = align256(off + 2 * bhn4);
   p.ws_bndk = off;

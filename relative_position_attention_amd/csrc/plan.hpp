@@ -43,13 +43,15 @@ struct Plan {
   SideLayout zq, zk;  // projection / offset-gradient layouts (query side, key side)
   bool need_qside = false;  // query-side offset gradients exist (AQ, bias or v)
   size_t t_size = 2, z_size = 2, g_size = 2;
+  bool dzq_f32 = false;    // query-side offset gradients in fp32 (bias without A^Q)
+  bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
 
   // ---- byte offsets inside z ----
-  size_t z_zq = 0, z_zk = 0, z_rowlo = 0, z_rowhi = 0, z_keylo = 0, z_keyhi = 0,
+  size_t z_gq = 0, z_gk = 0, z_zq = 0, z_zk = 0, z_rowlo = 0, z_rowhi = 0, z_keylo = 0, z_keyhi = 0,
          z_keymid = 0, z_bt = 0, z_bytes = 0;
   // ---- byte offsets inside ws (forward part) ----
-  size_t ws_gq = 0, ws_gk = 0, ws_beta_q = 0, ws_beta_k = 0, ws_beta_b = 0, ws_fold = 0,
+  size_t ws_beta_q = 0, ws_beta_k = 0, ws_beta_b = 0, ws_fold = 0,
          ws_atq = 0, ws_atk = 0, ws_fwd_end = 0;
   // ---- byte offsets inside ws (backward part, after ws_fwd_end) ----
   size_t ws_D = 0, ws_dqacc = 0, ws_dkacc = 0, ws_dz = 0, ws_bndq = 0, ws_bndk = 0,

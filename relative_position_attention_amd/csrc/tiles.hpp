@@ -110,4 +110,36 @@ __device__ __forceinline__ typename Mma<T>::frag frag_regs(const float (&v)[NB][
   }
 }
 
+// The rounding residue v - bf16(v) of the same values, as a bf16 fragment:
+// with frag_regs it forms a two-term (hi + lo) operand carrying about 16
+// significant bits, for products whose operand must not be cut to 8 bits.
+template <typename T, int NB>
+__device__ __forceinline__ typename Mma<T>::frag frag_regs_lo(const float (&v)[NB][4], int c) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = v[2 * c + (e >> 2)][e & 3];
+    f[e] = static_cast<bf16>(x - static_cast<float>(static_cast<bf16>(x)));
+  }
+  return f;
+}
+
+// An fp32 LDS run as an MFMA fragment (rounded once to bf16 for bf16 MFMA).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_f32(const float* p) {
+  if constexpr (sizeof(T) == 2) {
+    floatx4 a = *reinterpret_cast<const floatx4*>(p);
+    floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = static_cast<bf16>(a[e]);
+      f[e + 4] = static_cast<bf16>(b[e]);
+    }
+    return f;
+  } else {
+    return *p;
+  }
+}
+
 }  // namespace relpos

@@ -82,14 +82,16 @@ def test_saturated_tiles_small_delta():
     _case("shaw-D16-N1024", spec, arr)
 
 
-def test_bf16_outputs_within_one_ulp():
+def test_bf16_outputs_round_once():
+    # bf16 output mode writes the fp32-mode O (and dV, which does not depend
+    # on O) rounded once: within one bf16 unit in the last place.  (dQ and dK
+    # are not compared: their D = rowdot(dO, O) takes the rounded O as input.)
     spec, arr = scaled_config(2, B=1, H=2, N=256)
-    got = run_library(spec, arr, out_dtype="bf16")
-    ref = oracle.forward_backward(spec, arr)
-    for key in ("o", "dq", "dk", "dv"):
-        r = torch.from_numpy(ref[key]).to(torch.bfloat16).double().numpy()
-        ulp = np.abs(r) * 2.0 ** -7 + 1e-30
-        assert np.all(np.abs(got[key] - ref[key]) <= ulp + 2e-2), key
+    f32 = run_library(spec, arr, out_dtype="f32")
+    b16 = run_library(spec, arr, out_dtype="bf16")
+    for key in ("o", "dv"):
+        ulp = np.exp2(np.floor(np.log2(np.abs(f32[key]) + 1e-38)) - 7)
+        assert np.all(np.abs(b16[key] - f32[key]) <= ulp), key
 
 
 def test_recompute_projections_same_bits():
