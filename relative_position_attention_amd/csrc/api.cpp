@@ -274,6 +274,7 @@ int base_flags(const Plan& p) {
   if (p.aq) f |= F_ZQ;
   if (p.ak) f |= F_ZK;
   if (p.bias && !p.aq) f |= F_BT;
+  if (p.u) f |= F_U;
   if (p.causal) f |= F_CAUSAL;
   return f;
 }
@@ -324,8 +325,11 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   AttnArgs a = attn_args(p, in, z, ws);
   a.o = o;
   a.lse = lse;
-  RP_HIP(launch_attn_fwd(p.dtype == RELPOS_DTYPE_F32 ? 0 : 1,
-                         base_flags(p) | (p.split ? F_SPLIT : 0), a, p.B, s));
+  const int ff = base_flags(p) | (p.split ? F_SPLIT : 0);
+  if (p.dtype == RELPOS_DTYPE_F32)
+    RP_HIP(launch_attn_fwd(0, ff, a, p.B, s));
+  else
+    RP_HIP(launch_attn_fwd_bf16(ff, a, p.B, s));
   return RELPOS_OK;
 }
 
@@ -389,7 +393,8 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
-  RP_HIP(launch_attn_bwd_q(dt, bf | (p.need_qside ? F_DZQ : 0), a, p.B, s));
+  RP_HIP(launch_attn_bwd_q(dt, bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0), a,
+                           p.B, s));
   {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
@@ -408,6 +413,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.key_side = 0;
     f.causal = p.causal;
     f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
+    f.dz_f32 = p.dzq_f32;
     RP_HIP(launch_finalize(dt, f, p.BH, s));
   }
   if (p.need_qside) {

@@ -30,9 +30,9 @@ template <typename T, int F>
 __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   using M = Mma<T>;
   using Frag = typename M::frag;
-  // offset gradients of a bias without a query table are summed with
-  // cancellation (rows of dS sum to zero): they are kept in fp32
-  using GT = typename DzType<T, (F & F_BT) != 0>::type;
+  // offset gradients whose plain sums are needed (a scalar bias, or the
+  // Transformer-XL v term) cancel (rows of dS sum to zero): kept in fp32
+  using GT = typename DzType<T, (F & F_DZ32) != 0>::type;
   constexpr int E = M::E;
   constexpr int KS = M::KS;
   constexpr int NST = 64 / KS;
@@ -513,13 +513,14 @@ hipError_t launch_k(const AttnArgs& a, int B, hipStream_t s) {
 // The term combinations of the mechanisms: Shaw (ZQ), T5 (BT), DeBERTa
 // (ZQ+ZK), Transformer-XL (ZQ+U), each with and without the causal mask,
 // plus the plain and bias-with-key-table variants.
-#define RP_QFLAGS(X)                                      \
-  X(0) X(F_ZQ | F_DZQ) X(F_BT | F_DZQ) X(F_ZQ | F_ZK | F_DZQ) \
-  X(F_ZK) X(F_ZK | F_BT | F_DZQ)
+#define RP_QFLAGS(X)                                                         \
+  X(0) X(F_ZQ | F_DZQ) X(F_ZQ | F_ZK | F_DZQ) X(F_ZK)                        \
+  X(F_ZQ | F_DZQ | F_DZ32) X(F_BT | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_DZQ | F_DZ32) \
+  X(F_ZK | F_BT | F_DZQ | F_DZ32)
 
 template <typename T, int SPL>
 hipError_t dispatch_q(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZQ);
+  const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZQ | F_DZ32);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \

@@ -267,11 +267,10 @@ struct RedP {
 // boundary sums x A~[0], A~[2D] in fp32 (+ colsum u on the key side):
 // [RPA] App. B.1 table-gradient lemma, dQ = tau dS K + dZ^Q A^Q.  The bucket
 // fold is implicit: copies of one bucket multiply the same table row.
-template <typename T>
+template <typename T, typename GT>
 __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs f) {
   using M = Mma<T>;
   using Frag = typename M::frag;
-  using GT = typename Store<T>::G;
   constexpr int E = M::E, KS = M::KS, KC = RedP<T>::KC, LP = RedP<T>::P;
   __shared__ __attribute__((aligned(16))) T zs[64 * LP];
   __shared__ __attribute__((aligned(16))) T as[64 * LP];
@@ -680,9 +679,11 @@ hipError_t launch_rowdot(int dtype, int out_f32, const void* o, const void* dout
 hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s) {
   dim3 grid(nblk(f.N, 64), BH);
   if (dtype == 0)
-    hipLaunchKernelGGL(finalize_kernel<float>, grid, dim3(256), 0, s, f);
+    hipLaunchKernelGGL((finalize_kernel<float, float>), grid, dim3(256), 0, s, f);
+  else if (f.dz_f32)
+    hipLaunchKernelGGL((finalize_kernel<bf16, float>), grid, dim3(256), 0, s, f);
   else
-    hipLaunchKernelGGL(finalize_kernel<bf16>, grid, dim3(256), 0, s, f);
+    hipLaunchKernelGGL((finalize_kernel<bf16, bf16>), grid, dim3(256), 0, s, f);
   return hipGetLastError();
 }
 

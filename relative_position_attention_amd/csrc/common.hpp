@@ -161,6 +161,29 @@ __device__ __forceinline__ float wave_sum_g(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- buffer resources: 32-bit offsets, loads past `bytes` return zero (the
+// hardware range check replaces per-lane bounds branches)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every resource used here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(n), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float bloadf(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ _Float16 bloadh(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
 // Output element store (O, dQ, dK, dV) in the output dtype.
 __device__ __forceinline__ void store_out4(void* base, int64_t idx, bool f32, const float* v) {
   if (f32)

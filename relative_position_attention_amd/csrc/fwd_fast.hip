@@ -1,0 +1,416 @@
+// Forward attention kernel for bf16 inputs ([RPA] Table 9 "Attention"; the
+// forward of Algorithm 1).  [RPA] = "Fast and Exact Relative-Position
+// Attention via Structure-Aware Kernels" (arXiv 2611.01182).
+//
+// Layout.  A workgroup of 4 waves owns 128 consecutive queries (one
+// projection group); each wave owns 32 of them (two 16-query blocks), which
+// keeps a wave within 128 registers so four workgroups share a CU and the
+// MFMA work of some waves overlaps the softmax of others.  Key tiles of 64
+// keys stream through LDS, double buffered: K row-major, V transposed, and
+// (when a per-key relation term exists) the tile's per-key boundary entries.
+// All global reads are buffer loads: 32-bit offsets, and reads past a slice
+// return zero, so no lane branches on bounds.  Per tile and wave:
+//   S^T = K Q^T on 16x16x32 bf16 MFMA (each lane owns one query column and
+//   four consecutive keys per 16-key block);
+//   relation terms by tile region: a tile whose offsets delta = i - j all
+//   satisfy delta >= D or delta <= -D is saturated and adds one fp32 entry per
+//   query (folded into the exponent's offset) and one per key; band tiles
+//   read the per-pair projections Z ([RPA] §4.1, App. B saturated-tile lemma).
+//   Every pair with |delta| >= D takes the boundary entries whatever its tile,
+//   exactly as the backward passes do.
+//   Online softmax in base 2 with tau log2(e) folded into one FMA ([RPA]
+//   "Half-precision numerics"; [RPA] §3.1 Eq. (2)).  The running maximum is
+//   raised lazily: only when a tile's maximum exceeds it by more than 8
+//   (a factor 256) are O and the row sum rescaled; the result is the same
+//   exact quotient.
+//   O^T += V^T P^T on MFMA with P in registers (bf16, or a bf16 hi + lo pair
+//   under F_SPLIT).
+// The region of each tile is decided per wave from the wave's extreme offsets
+// before the loop (the three ranges of [RPA] §4.3.3).
+#include "relation.hpp"
+#include "tiles.hpp"
+
+namespace relpos {
+
+namespace {
+
+constexpr int QB = 2;              // 16-query blocks per wave
+constexpr int kWQ = 16 * QB;       // queries per wave
+constexpr int kBM = 4 * kWQ;       // queries per workgroup
+constexpr int kKP = 72;            // K tile pitch (bf16): 144-byte rows
+constexpr int kVP = 68;            // V^T tile pitch (bf16): 136-byte rows
+constexpr float kLazy = 8.f;       // rescale threshold, log2 units
+
+__device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+template <int F>
+__global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
+                                                          int xcd_map) {
+  constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
+  constexpr bool SPLIT = (F & F_SPLIT) != 0;
+  // per-key relation entries: with a key table (F_ZK) the band value and the
+  // two boundary values differ per key; with only the Transformer-XL u term
+  // they are one value u . k_j
+  constexpr bool KC = (F & (F_ZK | F_U)) != 0;
+  constexpr bool KC3 = (F & F_ZK) != 0;
+  __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kVP];
+  __shared__ __attribute__((aligned(16))) float skc[2][3][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = a.N, D = a.D;
+
+  // Work item.  Non-causal: items are head-major and, with xcd_map, each of
+  // the 8 XCDs (which receive workgroups round-robin) gets a contiguous range
+  // of items, so the query blocks of one head share one L2.  Causal: longest
+  // query blocks first.
+  int item = static_cast<int>(blockIdx.x);
+  if (xcd_map) {
+    const int q8 = total / 8, r8 = total % 8;
+    const int x = item % 8, slot = item / 8;
+    item = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + slot;
+  }
+  const int BH = total / nqb;
+  int bh, qblk;
+  if (CAUSAL) {
+    qblk = nqb - 1 - item / BH;
+    bh = item % BH;
+  } else {
+    bh = item / nqb;
+    qblk = item % nqb;
+  }
+  const int h = bh % a.H;
+  const int64_t tok = static_cast<int64_t>(bh) * N;
+  const int i0 = qblk * kBM;
+  const int iw = i0 + kWQ * wave;
+  const float sl2 = a.scale_log2;
+  const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
+  const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
+  const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
+
+  // queries of this lane: iw + 16 qb + c16 (rows past N load as zero)
+  bf16x8 qf[QB][2];
+  float rlo[QB], rhi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int i = iw + 16 * qb + c16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      qf[qb][c] = __builtin_bit_cast(bf16x8, bload16(rq, static_cast<uint32_t>(i * 128 + 64 * c + 16 * g)));
+    const bool ok = i < N;
+    rlo[qb] = ok ? a.rowlo[tok + i] : 0.f;
+    rhi[qb] = ok ? a.rowhi[tok + i] : 0.f;
+  }
+  GroupInfo giq = {0, 0, 0, 0};
+  if (F & F_ZQ) giq = a.gq[iw / kGroup];
+  const int gq0 = (iw / kGroup) * kGroup;
+  Rsrc rzq = rq, rzk = rq, rbt = rq;
+  if (F & F_ZQ)
+    rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,
+                    static_cast<uint64_t>(a.zq_bh) * 2);
+  if (F & F_ZK)
+    rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
+                    static_cast<uint64_t>(a.zk_bh) * 2);
+  if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+
+  // key tiles of the workgroup and of this wave
+  const int ilast_b = imin(N - 1, i0 + kBM - 1);
+  const int nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
+  const int nkt_w = CAUSAL ? imin(nkt, (iw + kWQ - 1) / 64 + 1) : nkt;
+  // region bounds from the wave's extreme offsets: tiles [0, n_hi) have
+  // delta >= D for every pair, tiles [t_lo, nkt_w) have delta <= -D
+  int n_hi = (iw - D - 63 >= 0) ? (iw - D - 63) / 64 + 1 : 0;
+  n_hi = imin(n_hi, nkt_w);
+  int t_lo = CAUSAL ? nkt_w : (iw + kWQ - 1 + D + 63) / 64;
+  t_lo = imax(n_hi, imin(t_lo, nkt_w));
+
+  float mu[QB], l[QB];
+  floatx4 o[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    mu[qb] = -INFINITY;
+    l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[qb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // tile staging: K rows (t>>3) and 32 + (t>>3), chunk t&7; V rows 2(t&31),
+  // 2(t&31)+1, chunk t>>5 (written transposed as bf16 pairs)
+  const int kr = tid >> 3, kc8 = (tid & 7) * 8;
+  const int vr = (tid & 31) * 2, vc8 = (tid >> 5) * 8;
+  uint4 tk[2], tv[2];
+  float tkc[3] = {0.f, 0.f, 0.f};
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      tk[u] = bload16(rk, static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2));
+      tv[u] = bload16(rv, static_cast<uint32_t>((j0 + vr + u) * 128 + vc8 * 2));
+    }
+    if (KC && tid < 64) {
+      const int j = j0 + tid;
+      const bool ok = j < N;
+      tkc[2] = ok ? a.keymid[tok + j] : 0.f;
+      if (KC3) {
+        tkc[0] = ok ? a.keylo[tok + j] : 0.f;
+        tkc[1] = ok ? a.keyhi[tok + j] : 0.f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<uint4*>(&sk[buf][(kr + 32 * u) * kKP + kc8]) = tk[u];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e of rows vr and vr + 1 as one bf16 pair
+      const uint32_t w0 = word4(tv[0], e >> 1), w1 = word4(tv[1], e >> 1);
+      const uint32_t pair = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                                    : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&sv[buf][(vc8 + e) * kVP + vr]) = pair;
+    }
+    if (KC && tid < 64) {
+      skc[buf][2][tid] = tkc[2];
+      if (KC3) {
+        skc[buf][0][tid] = tkc[0];
+        skc[buf][1][tid] = tkc[1];
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const int j0 = kt * 64;
+    if (kt + 1 < nkt) load_tile(j0 + 64);
+
+    if (kt < nkt_w) {
+      const bf16* Ks = sk[buf];
+      const bf16* Vt = sv[buf];
+      floatx4 s[QB][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kKP + 32 * c + 8 * g);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+        }
+      }
+
+      // ---- relation terms: s becomes S plus the per-pair terms (score
+      // units); off[qb] is the row's constant term (scaled) on saturated tiles
+      float off[QB];
+      if (kt < n_hi || kt >= t_lo) {
+        const int side = kt < n_hi ? 1 : 0;  // 1: delta >= D (row 2D), 0: delta <= -D
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) off[qb] = (side ? rhi[qb] : rlo[qb]) * sl2;
+        if (KC) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const floatx4 kx =
+                *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] += kx;
+          }
+        }
+      } else {
+        // band tile: per-pair terms; pairs with |delta| >= D take the
+        // boundary entries
+        GroupInfo gik = {0, 0, 0, 0};
+        const int gk0 = (j0 / kGroup) * kGroup;
+        if (F & F_ZK) gik = a.gk[j0 / kGroup];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          off[qb] = 0.f;
+          const int i = iw + 16 * qb + c16;
+          const bool iok = i < N;
+          const int zrow = giq.base + (i - gq0) * giq.pitch;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int j1 = j0 + 16 * kb + 4 * g;
+            float zq[4] = {0.f, 0.f, 0.f, 0.f};
+            if (F & F_ZQ) {
+              const int c0 = clamp_run((i - (j1 + 3) + D) - giq.slo + giq.pad, giq.pitch);
+              const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+              const halfx4 hv = __builtin_bit_cast(halfx4, w);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);  // descending
+            }
+            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int j = j1 + t;
+              const int dl = i - j;
+              const int jj = j - j0;
+              // boundary pairs: the row's entry plus the key's (one LDS read)
+              const float kedge = KC3 ? skc[buf][dl >= D ? 1 : 0][jj] : km[t];
+              float band = km[t] + zq[t];
+              if (F & F_ZK) {
+                const int cc = iclamp((dl + D) - gik.slo + gik.pad, 0, gik.pitch - 1);
+                const uint32_t offk =
+                    j < N ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + cc) * 2) : kOob;
+                band += static_cast<float>(bloadh(rzk, offk));
+              }
+              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            }
+          }
+        }
+      }
+      if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > iw)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int i = iw + 16 * qb + c16;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int j = j0 + 16 * kb + 4 * g + t;
+              if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = -INFINITY;
+            }
+        }
+      }
+
+      // ---- online softmax (base 2, lazy rescale)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[qb][kb][t]);
+        mx = wave_max_g(mx);
+        const float mxs = mx * sl2 + off[qb];  // scaled tile maximum
+        if (mxs > mu[qb] + kLazy) {
+          const float alpha = fast_exp2(mu[qb] - mxs);
+          mu[qb] = mxs;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
+        }
+        const float bias = off[qb] - mu[qb];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float p = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
+            s[qb][kb][t] = p;
+            ls += p;
+          }
+        l[qb] += ls;
+      }
+
+      // ---- O^T += V^T P^T (keys in the permuted order of frag_regs)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 pf[QB], pl[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[qb][2 * c + (e >> 2)][e & 3];
+            pf[qb][e] = static_cast<bf16>(x);
+            if (SPLIT) pl[qb][e] = static_cast<bf16>(x - static_cast<float>(pf[qb][e]));
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16* row = Vt + (16 * db + c16) * kVP + 32 * c + 4 * g;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+          bf16x8 vf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vf[e] = lo[e];
+            vf[e + 4] = hi[e];
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[qb][db], 0, 0, 0);
+            if (SPLIT)
+              o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], o[qb][db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // buffer buf ^ 1 was last read in iteration kt - 1, which every wave
+    // finished before the previous barrier
+    if (kt + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ls = wave_sum_g(l[qb]);
+    const int i = iw + 16 * qb + c16;
+    if (i >= N) continue;
+    const float inv = 1.f / ls;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      float vals[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv,
+                       o[qb][db][3] * inv};
+      store_out4(a.o, (tok + i) * 64 + 16 * db + 4 * g, a.out_f32 != 0, vals);
+    }
+    if (g == 0) a.lse[tok + i] = mu[qb] * kLn2 + logf(ls);
+  }
+}
+
+template <int F>
+hipError_t launch_fast(const AttnArgs& a, int B, hipStream_t s) {
+  const int nqb = (a.N + kBM - 1) / kBM;
+  const int total = nqb * B * a.H;
+  const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
+  hipLaunchKernelGGL((attn_fwd_fast<F>), dim3(total), dim3(256), 0, s, a, nqb, total, xcd_map);
+  return hipGetLastError();
+}
+
+template <int SPL>
+hipError_t dispatch_fast(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  const int f = flags & (F_ZQ | F_ZK | F_BT | F_U | F_CAUSAL);
+  switch (f) {
+#define RP_CASE(X)                                        \
+  case X:                                                 \
+    return launch_fast<(X) | SPL>(a, B, s);               \
+  case (X) | F_CAUSAL:                                    \
+    return launch_fast<(X) | F_CAUSAL | SPL>(a, B, s);
+    RP_CASE(0)
+    RP_CASE(F_ZQ)
+    RP_CASE(F_ZK)
+    RP_CASE(F_BT)
+    RP_CASE(F_ZQ | F_ZK)
+    RP_CASE(F_ZK | F_BT)
+    RP_CASE(F_U)
+    RP_CASE(F_ZQ | F_U)
+    RP_CASE(F_ZK | F_U)
+    RP_CASE(F_BT | F_U)
+    RP_CASE(F_ZQ | F_ZK | F_U)
+    RP_CASE(F_ZK | F_BT | F_U)
+#undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  if (flags & F_SPLIT) return dispatch_fast<F_SPLIT>(flags, a, B, s);
+  return dispatch_fast<0>(flags, a, B, s);
+}
+
+}  // namespace relpos

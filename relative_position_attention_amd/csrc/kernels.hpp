@@ -22,6 +22,7 @@ enum : int {
   F_DZK = 32,    // backward: key-side offset gradients (A^K present)
   F_U = 64,      // backward: key column sums of G (Transformer-XL u term)
   F_SPLIT = 128,  // bf16: P and G enter their MFMA products as bf16 hi + lo
+  F_DZ32 = 256,   // backward: query-side offset gradients stored in fp32
 };
 
 struct AttnArgs {
@@ -59,6 +60,8 @@ struct AttnArgs {
 
 // dtype: 0 = fp32 inputs, 1 = bf16 inputs.  Return hipError_t of the launch.
 hipError_t launch_attn_fwd(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+// bf16 forward: 64 queries per wave, 256 per workgroup (fwd_fast.hip)
+hipError_t launch_attn_fwd_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_bwd_q(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_bwd_k(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
 
@@ -163,6 +166,7 @@ struct FinalizeArgs {
   const void* u;        // [H, 64]
   void* out;            // out dtype
   int N, H, D, S, key_side, causal, out_f32;
+  int dz_f32;  // entries are fp32
 };
 hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s);
 

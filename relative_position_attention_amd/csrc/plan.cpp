@@ -271,8 +271,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     detail = "split_operands must be 0 or 1";
     return RELPOS_E_INVALID_ARG;
   }
-  if (!std::isfinite(desc->scale)) {
-    detail = "scale must be finite";
+  if (!std::isfinite(desc->scale) || !(desc->scale > 0.f)) {
+    detail = "scale must be finite and positive";
     return RELPOS_E_INVALID_ARG;
   }
   p = Plan();
@@ -293,7 +293,9 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.t_size = desc->dtype == RELPOS_DTYPE_F32 ? 4 : 2;
   p.z_size = p.t_size;  // fp16 projections for bf16 inputs ([RPA] "Half-precision numerics")
   p.g_size = p.t_size;  // offset gradients in the input precision
-  p.dzq_f32 = p.bias && !p.aq;  // ... except a bias alone: fp32 (sums cancel)
+  // ... except where their plain sums are needed (a bias, or the v term):
+  // fp32, since those sums cancel
+  p.dzq_f32 = p.bias || p.v;
   p.split = desc->split_operands != 0 && p.dtype == RELPOS_DTYPE_BF16;
   bool any_table = p.aq || p.ak || p.bias;
   if (any_table && p.R < 1) {

@@ -5,8 +5,10 @@
 // Offset-aware tiles ([RPA] §4.1 "Constant-Range Reuse", §4.3.1, App. B.2
 // saturated-tile lemma): a tile whose offsets all satisfy delta >= D
 // (SAT_HI) or delta <= -D (SAT_LO) reads one precomputed entry per query and
-// one per key; only BAND tiles read the per-pair projections.  Inside a band
-// tile, pairs with delta > D or delta < -D still take the boundary entries.
+// one per key; only BAND tiles read the per-pair projections.  Every pair
+// with |delta| >= D takes the fp32 boundary entries, in every kind of tile, so
+// the value of a score does not depend on how its tile was classified (the
+// forward and both backward passes classify tiles differently).
 #pragma once
 
 #include "common.hpp"
@@ -66,7 +68,7 @@ __device__ __forceinline__ void relation_qrow(const AttnArgs& a, int64_t tok, in
       }
     }
     if (F & F_BT) band += a.bt[h * a.S + iclamp(dl + D, 0, 2 * D)];
-    acc[t] += dl > D ? (rhi + kh[t]) : (dl < -D ? (rlo + kl[t]) : band);
+    acc[t] += dl >= D ? (rhi + kh[t]) : (dl <= -D ? (rlo + kl[t]) : band);
   }
 }
 
@@ -111,7 +113,7 @@ __device__ __forceinline__ void relation_krow(const AttnArgs& a, int64_t tok, in
       }
     }
     if (F & F_BT) band += a.bt[h * a.S + iclamp(dl + D, 0, 2 * D)];
-    acc[t] += dl > D ? (rhi4[t] + khi) : (dl < -D ? (rlo4[t] + klo) : band);
+    acc[t] += dl >= D ? (rhi4[t] + khi) : (dl <= -D ? (rlo4[t] + klo) : band);
   }
 }
 

@@ -66,13 +66,14 @@ def test_mask_variants(kind, causal):
     _case(f"{kind}-causal{int(causal)}", spec, arr)
 
 
-@pytest.mark.parametrize("N", [1, 2, 17, 64, 129])
-def test_small_and_ragged(N):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 129, 200])
+def test_small_and_ragged(N, dtype):
     for kind in ("shaw", "t5", "deberta", "txl"):
         for causal in (False, True):
-            spec, arr = make_problem(kind=kind, B=1, H=2, N=N, dtype="f32", seed=N + 3,
+            spec, arr = make_problem(kind=kind, B=1, H=2, N=N, dtype=dtype, seed=N + 3,
                                      causal=causal, clip=5, d_model=128)
-            _case(f"{kind}-N{N}-c{int(causal)}", spec, arr)
+            _case(f"{kind}-{dtype}-N{N}-c{int(causal)}", spec, arr)
 
 
 def test_saturated_tiles_small_delta():
