@@ -19,6 +19,64 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Host plans are cached per thread, keyed by the descriptor's contents (the
+// explicit map rows included) and the shape: building one evaluates the map
+// over every offset, far more host time than enqueuing the kernels.
+struct PlanCache {
+  std::vector<std::pair<std::string, Plan>> entries;  // most recent last
+};
+thread_local PlanCache g_plans;
+constexpr size_t kPlanCacheSize = 16;
+
+std::string plan_key(const relpos_desc* d, const relpos_shape* sh) {
+  std::string key(reinterpret_cast<const char*>(sh), sizeof(relpos_shape));
+  relpos_desc copy = *d;
+  copy.map.explicit_rows = nullptr;
+  key.append(reinterpret_cast<const char*>(&copy), sizeof copy);
+  if (d->map.kind == RELPOS_MAP_EXPLICIT && d->map.explicit_rows != nullptr && d->map.clip >= 0)
+    key.append(reinterpret_cast<const char*>(d->map.explicit_rows),
+               sizeof(int32_t) * (2 * static_cast<size_t>(d->map.clip) + 1));
+  return key;
+}
+
+// The plan of (desc, shape), from the cache or built; nullptr on error.
+const Plan* get_plan(const relpos_desc* desc, const relpos_shape* shape, int& rc) {
+  rc = RELPOS_OK;
+  if (desc == nullptr || shape == nullptr) {
+    rc = RELPOS_E_INVALID_ARG;
+    g_last_error = "null descriptor or shape";
+    return nullptr;
+  }
+  // the key needs a readable descriptor: validate the ABI version first
+  if (desc->abi_version != RELPOS_ABI_VERSION) {
+    rc = RELPOS_E_ABI;
+    g_last_error = "abi_version mismatch";
+    return nullptr;
+  }
+  const std::string key = plan_key(desc, shape);
+  auto& E = g_plans.entries;
+  for (size_t k = 0; k < E.size(); ++k) {
+    if (E[k].first == key) {
+      if (k + 1 != E.size()) {
+        auto hit = std::move(E[k]);
+        E.erase(E.begin() + k);
+        E.push_back(std::move(hit));
+      }
+      return &E.back().second;
+    }
+  }
+  Plan p;
+  std::string detail;
+  rc = make_plan(desc, shape, p, detail);
+  if (rc != RELPOS_OK) {
+    g_last_error = detail;
+    return nullptr;
+  }
+  if (E.size() >= kPlanCacheSize) E.erase(E.begin());
+  E.emplace_back(key, std::move(p));
+  return &E.back().second;
+}
+
 int fail(int code, const std::string& detail) {
   g_last_error = detail;
   return code;
@@ -281,10 +339,10 @@ int base_flags(const Plan& p) {
 
 int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
                 void* z, size_t z_bytes, void* ws, size_t ws_bytes, hipStream_t s) {
-  Plan p;
-  std::string detail;
-  int rc = make_plan(desc, shape, p, detail);
-  if (rc != RELPOS_OK) return fail(rc, detail);
+  int rc;
+  const Plan* pp = get_plan(desc, shape, rc);
+  if (pp == nullptr) return rc;
+  const Plan& p = *pp;
   if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
   if (z == nullptr || z_bytes < p.z_bytes) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "z too small");
   if (ws == nullptr || ws_bytes < p.ws_fwd_end)
@@ -299,10 +357,10 @@ int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos
 int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
             const void* zc, size_t z_bytes, void* o, float* lse, void* ws, size_t ws_bytes,
             hipStream_t s) {
-  Plan p;
-  std::string detail;
-  int rc = make_plan(desc, shape, p, detail);
-  if (rc != RELPOS_OK) return fail(rc, detail);
+  int rc;
+  const Plan* pp = get_plan(desc, shape, rc);
+  if (pp == nullptr) return rc;
+  const Plan& p = *pp;
   if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
   if (o == nullptr || lse == nullptr || !aligned16(o) || !aligned16(lse))
     return fail(o && lse ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG, "o / lse");
@@ -336,10 +394,10 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
 int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
             const void* zc, size_t z_bytes, const void* o, const float* lse, const void* dout,
             relpos_grads* gr, void* ws, size_t ws_bytes, hipStream_t s) {
-  Plan p;
-  std::string detail;
-  int rc = make_plan(desc, shape, p, detail);
-  if (rc != RELPOS_OK) return fail(rc, detail);
+  int rc;
+  const Plan* pp = get_plan(desc, shape, rc);
+  if (pp == nullptr) return rc;
+  const Plan& p = *pp;
   if ((rc = check_inputs(p, in)) != RELPOS_OK) return rc;
   if (!o || !lse || !dout || !gr) return fail(RELPOS_E_INVALID_ARG, "null o, lse, dout or grads");
   if (!aligned16(o) || !aligned16(dout)) return fail(RELPOS_E_MISALIGNED, "o / dout misaligned");
@@ -372,6 +430,8 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   float* colsum = at_off<float>(ws, p.ws_colsum);
   float* p1 = at_off<float>(ws, p.ws_p1);
   float* p2 = at_off<float>(ws, p.ws_p2);
+  float* db = at_off<float>(ws, p.ws_db);
+  float* red = at_off<float>(ws, p.ws_red);
   const int64_t rows = static_cast<int64_t>(p.BH) * p.N;
 
   // Preprocessing: D = rowdot(dO, O)
@@ -393,8 +453,11 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
-  RP_HIP(launch_attn_bwd_q(dt, bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0), a,
-                           p.B, s));
+  const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0);
+  if (dt == 0)
+    RP_HIP(launch_attn_bwd_q(dt, qflags, a, p.B, s));
+  else
+    RP_HIP(launch_bwd_q_bf16(qflags, a, p.B, s));
   {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
@@ -414,7 +477,10 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.causal = p.causal;
     f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
     f.dz_f32 = p.dzq_f32;
-    RP_HIP(launch_finalize(dt, f, p.BH, s));
+    if (dt == 0)
+      RP_HIP(launch_finalize(dt, f, p.BH, s));
+    else
+      RP_HIP(launch_finalize_bf16(f, p.BH, s));
   }
   if (p.need_qside) {
     PartialArgs pa;
@@ -434,7 +500,10 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.key_side = 0;
     pa.causal = p.causal;
     pa.dz_f32 = p.dzq_f32;
-    RP_HIP(launch_partials(dt, pa, s));
+    if (dt == 0)
+      RP_HIP(launch_partials(dt, pa, s));
+    else
+      RP_HIP(launch_partials_bf16(pa, s));
     if (p.aq) {
       FoldArgs fa;
       fa.p1 = p1;
@@ -452,9 +521,10 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
       fa.shared = p.aq_shared;
       RP_HIP(launch_fold_table(dt, fa, s));
     }
+    if (p.bias || p.v) RP_HIP(launch_p2_sum(p2, db, p.H, p.S, p.nchunk, s));
     if (p.bias) {
       FoldBiasArgs fb;
-      fb.p2 = p2;
+      fb.db = db;
       fb.fold = fold_ptr(p, ws, 2);
       fb.out = gr->dbias;
       fb.row_stride = desc->bias_row_stride;
@@ -462,24 +532,27 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
       fb.H = p.H;
       fb.R = p.R;
       fb.S = p.S;
-      fb.nchunk = p.nchunk;
       RP_HIP(launch_fold_bias(fb, s));
     }
     if (p.v) {
       DvArgs dv;
-      dv.p2 = p2;
+      dv.db = db;
       dv.atq = at_off<char>(ws, p.ws_atq);
       dv.at_shared = p.aq_shared;
+      dv.part = red;
       dv.out = gr->dvbias;
       dv.H = p.H;
       dv.S = p.S;
-      dv.nchunk = p.nchunk;
       RP_HIP(launch_dv(dt, dv, s));
     }
   }
 
   // Key-parallel pass, then the key reduction
-  RP_HIP(launch_attn_bwd_k(dt, bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0), a, p.B, s));
+  const int kflags = bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0);
+  if (dt == 0)
+    RP_HIP(launch_attn_bwd_k(dt, kflags, a, p.B, s));
+  else
+    RP_HIP(launch_bwd_k_bf16(kflags, a, p.B, s));
   {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
@@ -500,7 +573,10 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.key_side = 1;
     f.causal = p.causal;
     f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
-    RP_HIP(launch_finalize(dt, f, p.BH, s));
+    if (dt == 0)
+      RP_HIP(launch_finalize(dt, f, p.BH, s));
+    else
+      RP_HIP(launch_finalize_bf16(f, p.BH, s));
   }
   if (p.ak) {
     PartialArgs pa;
@@ -520,7 +596,10 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.key_side = 1;
     pa.causal = p.causal;
     pa.dz_f32 = 0;
-    RP_HIP(launch_partials(dt, pa, s));
+    if (dt == 0)
+      RP_HIP(launch_partials(dt, pa, s));
+    else
+      RP_HIP(launch_partials_bf16(pa, s));
     FoldArgs fa;
     fa.p1 = p1;
     fa.p2 = nullptr;
@@ -541,6 +620,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     DuArgs du;
     du.colsum = colsum;
     du.k = in->k;
+    du.part = red;
     du.out = gr->du;
     du.B = p.B;
     du.H = p.H;
@@ -560,10 +640,10 @@ extern "C" {
 int relpos_plan_sizes(const relpos_desc* desc, const relpos_shape* shape, relpos_sizes* out) {
   try {
     if (out == nullptr) return fail(RELPOS_E_INVALID_ARG, "null output");
-    Plan p;
-    std::string detail;
-    int rc = make_plan(desc, shape, p, detail);
-    if (rc != RELPOS_OK) return fail(rc, detail);
+    int rc;
+    const Plan* pp = get_plan(desc, shape, rc);
+    if (pp == nullptr) return rc;
+    const Plan& p = *pp;
     out->z_bytes = p.z_bytes;
     out->fwd_ws_bytes = p.ws_fwd_end;  // relpos_project; relpos_attn_fwd with z needs none
     out->fwd_ws_bytes_noz = p.ws_fwd_end + p.z_bytes;
@@ -584,10 +664,10 @@ int relpos_plan_sizes(const relpos_desc* desc, const relpos_shape* shape, relpos
 int relpos_plan_rows(const relpos_desc* desc, const relpos_shape* shape, int32_t which,
                      int32_t* rows_out, int32_t cap) {
   try {
-    Plan p;
-    std::string detail;
-    int rc = make_plan(desc, shape, p, detail);
-    if (rc != RELPOS_OK) return fail(rc, detail);
+    int rc;
+    const Plan* pp = get_plan(desc, shape, rc);
+    if (pp == nullptr) return rc;
+    const Plan& p = *pp;
     const std::vector<int32_t>* b = which == 0 ? &p.beta_q : which == 1 ? &p.beta_k
                                      : which == 2 ? &p.beta_b : nullptr;
     if (b == nullptr || rows_out == nullptr) return fail(RELPOS_E_INVALID_ARG, "bad table index");

@@ -553,47 +553,80 @@ __global__ __launch_bounds__(64) void fold_table_kernel(FoldArgs f, int dtype) {
   f.out[r * f.row_stride + ht * f.head_stride + d] = sum;
 }
 
-__global__ __launch_bounds__(64) void fold_bias_kernel(FoldBiasArgs f) {
-  const int r = blockIdx.x;
-  const int sa = f.fold[2 * r], sb = f.fold[2 * r + 1];
-  for (int h = threadIdx.x; h < f.H; h += 64) {
-    float sum = 0.f;
-    for (int s = sa; s <= sb; ++s)
-      for (int c = 0; c < f.nchunk; ++c) sum += f.p2[(static_cast<int64_t>(h) * f.nchunk + c) * f.S + s];
-    f.out[r * f.row_stride + h * f.head_stride] = sum;
-  }
+// db[h][s] = sum over chunks c (ascending) of P2[h][c][s]
+__global__ __launch_bounds__(256) void p2_sum_kernel(const float* p2, float* db, int H, int S,
+                                                     int nchunk) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H * S) return;
+  const int h = idx / S, s = idx % S;
+  float sum = 0.f;
+  for (int c = 0; c < nchunk; ++c) sum += p2[(static_cast<int64_t>(h) * nchunk + c) * S + s];
+  db[idx] = sum;
 }
 
+// dbias[r, h] = sum over the copies s of row r (ascending) of db[h][s]: the
+// bucket fold of [RPA] App. B.1 (bucket-copy lemma), db = E^T db~
+__global__ __launch_bounds__(256) void fold_bias_kernel(FoldBiasArgs f) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= f.R * f.H) return;
+  const int r = idx / f.H, h = idx % f.H;
+  const int sa = f.fold[2 * r], sb = f.fold[2 * r + 1];
+  float sum = 0.f;
+  for (int s = sa; s <= sb; ++s) sum += f.db[static_cast<int64_t>(h) * f.S + s];
+  f.out[r * f.row_stride + h * f.head_stride] = sum;
+}
+
+constexpr int kSplit = 64;  // partial sums per head in the two-phase row sums
+
+// dv, first phase: part[h][sp][d] = sum over the rows s of split sp of
+// db[h][s] A~^Q[s][d] (fixed order: stride-4 rows per quarter, quarters summed
+// in order)
 template <typename T>
-__global__ __launch_bounds__(256) void dv_kernel(DvArgs a) {
+__global__ __launch_bounds__(256) void dv_part_kernel(DvArgs a) {
   __shared__ float part[4][64];
-  const int h = blockIdx.x, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int h = blockIdx.x, sp = blockIdx.y, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int per = (a.S + kSplit - 1) / kSplit;
+  const int s0 = sp * per, s1 = imin(a.S, s0 + per);
   const T* at = reinterpret_cast<const T*>(a.atq) +
                 static_cast<int64_t>(a.at_shared ? 0 : h) * a.S * 64;
   float sum = 0.f;
-  for (int s = q; s < a.S; s += 4) {
-    float db = 0.f;
-    for (int c = 0; c < a.nchunk; ++c) db += a.p2[(static_cast<int64_t>(h) * a.nchunk + c) * a.S + s];
-    sum += db * to_f(at[static_cast<int64_t>(s) * 64 + d]);
-  }
+  for (int s = s0 + q; s < s1; s += 4)
+    sum += a.db[static_cast<int64_t>(h) * a.S + s] * to_f(at[static_cast<int64_t>(s) * 64 + d]);
   part[q][d] = sum;
   __syncthreads();
-  if (q == 0) a.out[h * 64 + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  if (q == 0)
+    a.part[(static_cast<int64_t>(h) * kSplit + sp) * 64 + d] =
+        ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
 }
 
+// du, first phase: part[h][sp][d] = sum over the tokens (b, j) of split sp of
+// colsum[b, h, j] k[b, h, j, d]
 template <typename T>
-__global__ __launch_bounds__(256) void du_kernel(DuArgs a) {
+__global__ __launch_bounds__(256) void du_part_kernel(DuArgs a) {
   __shared__ float part[4][64];
-  const int h = blockIdx.x, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int h = blockIdx.x, sp = blockIdx.y, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t total = static_cast<int64_t>(a.B) * a.N;
+  const int64_t per = (total + kSplit - 1) / kSplit;
+  const int64_t t0 = sp * per, t1 = t0 + per < total ? t0 + per : total;
   float sum = 0.f;
-  for (int b = 0; b < a.B; ++b) {
-    const int64_t tok = (static_cast<int64_t>(b) * a.H + h) * a.N;
-    const T* k = reinterpret_cast<const T*>(a.k) + tok * 64;
-    for (int j = q; j < a.N; j += 4) sum += a.colsum[tok + j] * to_f(k[static_cast<int64_t>(j) * 64 + d]);
+  for (int64_t t = t0 + q; t < t1; t += 4) {
+    const int64_t b = t / a.N, j = t % a.N;
+    const int64_t row = (b * a.H + h) * a.N + j;
+    sum += a.colsum[row] * to_f(reinterpret_cast<const T*>(a.k)[row * 64 + d]);
   }
   part[q][d] = sum;
   __syncthreads();
-  if (q == 0) a.out[h * 64 + d] = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  if (q == 0)
+    a.part[(static_cast<int64_t>(h) * kSplit + sp) * 64 + d] =
+        ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+}
+
+// second phase: out[h][d] = sum over splits (ascending) of part[h][sp][d]
+__global__ __launch_bounds__(64) void split_sum_kernel(const float* part, float* out) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  float sum = 0.f;
+  for (int sp = 0; sp < kSplit; ++sp) sum += part[(static_cast<int64_t>(h) * kSplit + sp) * 64 + d];
+  out[h * 64 + d] = sum;
 }
 
 inline unsigned nblk(int64_t n, int b) { return static_cast<unsigned>((n + b - 1) / b); }
@@ -703,24 +736,33 @@ hipError_t launch_fold_table(int dtype, const FoldArgs& f, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_p2_sum(const float* p2, float* db, int H, int S, int nchunk, hipStream_t s) {
+  hipLaunchKernelGGL(p2_sum_kernel, dim3(nblk(static_cast<int64_t>(H) * S, 256)), dim3(256), 0, s,
+                     p2, db, H, S, nchunk);
+  return hipGetLastError();
+}
+
 hipError_t launch_fold_bias(const FoldBiasArgs& f, hipStream_t s) {
-  hipLaunchKernelGGL(fold_bias_kernel, dim3(f.R), dim3(64), 0, s, f);
+  hipLaunchKernelGGL(fold_bias_kernel, dim3(nblk(static_cast<int64_t>(f.R) * f.H, 256)), dim3(256),
+                     0, s, f);
   return hipGetLastError();
 }
 
 hipError_t launch_dv(int dtype, const DvArgs& a, hipStream_t s) {
   if (dtype == 0)
-    hipLaunchKernelGGL(dv_kernel<float>, dim3(a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(dv_part_kernel<float>, dim3(a.H, kSplit), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(dv_kernel<bf16>, dim3(a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(dv_part_kernel<bf16>, dim3(a.H, kSplit), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(split_sum_kernel, dim3(a.H), dim3(64), 0, s, a.part, a.out);
   return hipGetLastError();
 }
 
 hipError_t launch_du(int dtype, const DuArgs& a, hipStream_t s) {
   if (dtype == 0)
-    hipLaunchKernelGGL(du_kernel<float>, dim3(a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(du_part_kernel<float>, dim3(a.H, kSplit), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(du_kernel<bf16>, dim3(a.H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(du_part_kernel<bf16>, dim3(a.H, kSplit), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(split_sum_kernel, dim3(a.H), dim3(64), 0, s, a.part, a.out);
   return hipGetLastError();
 }
 

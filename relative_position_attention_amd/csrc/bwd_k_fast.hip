@@ -1,0 +1,396 @@
+// Key-parallel backward pass for bf16 inputs ([RPA] Table 9 "Key-parallel
+// pass", Algorithm 2).  [RPA] = "Fast and Exact Relative-Position Attention
+// via Structure-Aware Kernels" (arXiv 2611.01182).
+//
+// A workgroup of 4 waves owns 128 keys (one projection group), 32 per wave.
+// Query tiles of 32 queries (Q, dO row-major, and per query L, D and the two
+// boundary entries) stream through double-buffered LDS; the short tile keeps
+// a wave's scores, score gradients and four accumulators within 256
+// registers.  Per tile and wave:
+//   S = Q K^T and dP = dO V^T on MFMA (A from LDS rows, K and V of the
+//   wave's keys in registers), each lane owning one key column and four
+//   consecutive queries per 16-query block;
+//   relation terms exactly as the forward (same boundary-entry rule);
+//   P = exp2(S tau log2 e - L log2 e), G = tau P (dP - D);
+//   dV^T += dO^T P and dK^T += Q^T G on MFMA (dO^T and Q^T read with the
+//   transposing LDS read; P and G as bf16, or bf16 hi + lo under F_SPLIT).
+// Key offset gradients ([RPA] §4.2): a band pair writes G to
+// dZ~^K[j, delta + D] (single writer, aligned 4-entry runs); pairs with
+// |delta| >= D add into two fp32 per-key boundary sums; with the
+// Transformer-XL u term the column sums of G are kept too.  No atomics.
+#include "relation.hpp"
+#include "tiles.hpp"
+
+namespace relpos {
+
+namespace {
+
+constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
+constexpr int kT = 32;  // queries per tile
+
+template <int F>
+__global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int total, int xcd_map) {
+  constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
+  constexpr bool SPLIT = (F & F_SPLIT) != 0;
+  constexpr bool DZ = (F & F_DZK) != 0;
+  constexpr bool CS = (F & F_U) != 0;
+  constexpr bool KC = (F & (F_ZK | F_U)) != 0;
+  __shared__ __attribute__((aligned(16))) bf16 sq[2][kT * kP];
+  __shared__ __attribute__((aligned(16))) bf16 sd[2][kT * kP];
+  __shared__ __attribute__((aligned(16))) float sqs[2][4][kT];  // l2, D, rowlo, rowhi
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = a.N, D = a.D;
+
+  int item = static_cast<int>(blockIdx.x);
+  if (xcd_map) {
+    const int q8 = total / 8, r8 = total % 8;
+    const int x = item % 8, slot = item / 8;
+    item = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + slot;
+  }
+  const int BH = total / nkb;
+  int bh, kblk;
+  if (CAUSAL) {
+    // causal: the first key blocks see the most queries
+    kblk = item / BH;
+    bh = item % BH;
+  } else {
+    bh = item / nkb;
+    kblk = item % nkb;
+  }
+  const int h = bh % a.H;
+  const int64_t tok = static_cast<int64_t>(bh) * N;
+  const int j0b = kblk * 128;
+  const int jw = j0b + 32 * wave;
+  const float sl2 = a.scale_log2, tau = a.scale;
+  const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
+  const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
+  const Rsrc rdo = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + tok * 64, slice_bytes);
+  const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
+
+  // keys of this lane: jw + 16 kb + c16
+  bf16x8 kf[2][2], vf[2][2];
+  float klo[2], khi[2], kmid[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = jw + 16 * kb + c16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t off = static_cast<uint32_t>(j * 128 + 64 * c + 16 * g);
+      kf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rk, off));
+      vf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rv, off));
+    }
+    const bool ok = j < N;
+    klo[kb] = (KC && ok) ? a.keylo[tok + j] : 0.f;
+    khi[kb] = (KC && ok) ? a.keyhi[tok + j] : 0.f;
+    kmid[kb] = (KC && ok) ? a.keymid[tok + j] : 0.f;
+  }
+  GroupInfo gik = {0, 0, 0, 0};
+  if ((F & F_ZK) || DZ) gik = a.gk[j0b / kGroup];
+  Rsrc rzq = rq, rzk = rq, rbt = rq;
+  if (F & F_ZQ)
+    rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,
+                    static_cast<uint64_t>(a.zq_bh) * 2);
+  if (F & F_ZK)
+    rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
+                    static_cast<uint64_t>(a.zk_bh) * 2);
+  if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+
+  // query tiles: causal starts at the block's first key; the wave's tiles
+  // before its own first key are fully masked and skipped.  Regions from the
+  // wave's extreme offsets: [it_first, n_lo) all delta <= -D, [t_hi, nqt) all
+  // delta >= D.
+  const int nqt = (N + kT - 1) / kT;
+  const int it0 = CAUSAL ? j0b / kT : 0;
+  const int itw = CAUSAL ? jw / kT : 0;
+  int n_lo = (jw - D - (kT - 1) >= 0) ? (jw - D - (kT - 1)) / kT + 1 : 0;
+  n_lo = CAUSAL ? itw : imax(itw, imin(n_lo, nqt));
+  int t_hi = (jw + 31 + D + kT - 1) / kT;
+  t_hi = imax(n_lo, imin(t_hi, nqt));
+
+  floatx4 dk[2][4], dv[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dk[kb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dv[kb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  float blo[2] = {0.f, 0.f}, bhi[2] = {0.f, 0.f}, csum[2] = {0.f, 0.f};
+
+  const int kr = tid >> 3, kc8 = (tid & 7) * 8;
+  uint4 tq, td;
+  float tqs[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_tile = [&](int i0) {
+    const uint32_t off = static_cast<uint32_t>((i0 + kr) * 128 + kc8 * 2);
+    tq = bload16(rq, off);
+    td = bload16(rdo, off);
+    if (tid < kT) {
+      const int i = i0 + tid;
+      const bool ok = i < N;
+      tqs[0] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
+      tqs[1] = ok ? a.dvec[tok + i] : 0.f;
+      tqs[2] = ok ? a.rowlo[tok + i] : 0.f;
+      tqs[3] = ok ? a.rowhi[tok + i] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    *reinterpret_cast<uint4*>(&sq[buf][kr * kP + kc8]) = tq;
+    *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = td;
+    if (tid < kT) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sqs[buf][x][tid] = tqs[x];
+    }
+  };
+
+  if (it0 < nqt) {
+    load_tile(it0 * kT);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = it0; it < nqt; ++it) {
+    const int buf = (it - it0) & 1;
+    const int i0 = it * kT;
+    if (it + 1 < nqt) load_tile(i0 + kT);
+
+    if (it >= itw) {
+      const bf16* Qs = sq[buf];
+      const bf16* Ds = sd[buf];
+      floatx4 s[2][2], dp[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + c16) * kP + 32 * c + 8 * g);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + (16 * qb + c16) * kP + 32 * c + 8 * g);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kb][c], s[qb][kb], 0, 0, 0);
+            dp[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[kb][c], dp[qb][kb], 0, 0, 0);
+          }
+        }
+      }
+
+      const bool sat_lo = it < n_lo, sat_hi = it >= t_hi;
+      const bool need_mask = (i0 + kT > N) || (jw + 32 > N) || (CAUSAL && i0 < jw + 31);
+      GroupInfo giq = {0, 0, 0, 0};
+      if (F & F_ZQ) giq = a.gq[i0 / kGroup];
+      const int gq0 = (i0 / kGroup) * kGroup;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int i1 = i0 + 16 * qb + 4 * g;
+        const int qo = 16 * qb + 4 * g;
+        const floatx4 ql2 = *reinterpret_cast<const floatx4*>(&sqs[buf][0][qo]);
+        const floatx4 qdd = *reinterpret_cast<const floatx4*>(&sqs[buf][1][qo]);
+        const floatx4 qrl = *reinterpret_cast<const floatx4*>(&sqs[buf][2][qo]);
+        const floatx4 qrh = *reinterpret_cast<const floatx4*>(&sqs[buf][3][qo]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int j = jw + 16 * kb + c16;
+          float rel[4];
+          if (sat_lo || sat_hi) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) rel[t] = sat_hi ? (qrh[t] + khi[kb]) : (qrl[t] + klo[kb]);
+          } else {
+            float zk[4] = {0.f, 0.f, 0.f, 0.f};
+            if (F & F_ZK) {
+              const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
+              const uint32_t offk = j < N
+                  ? static_cast<uint32_t>((gik.base + (j - j0b) * gik.pitch + c0) * 2) : kOob;
+              const halfx4 hv = __builtin_bit_cast(halfx4, bload8(rzk, offk));
+#pragma unroll
+              for (int t = 0; t < 4; ++t) zk[t] = static_cast<float>(hv[t]);  // ascending
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int i = i1 + t;
+              const int dl = i - j;
+              float band = kmid[kb] + zk[t];
+              if (F & F_ZQ) {
+                const int cc = iclamp((dl + D) - giq.slo + giq.pad, 0, giq.pitch - 1);
+                const uint32_t offq =
+                    i < N ? static_cast<uint32_t>((giq.base + (i - gq0) * giq.pitch + cc) * 2) : kOob;
+                band += static_cast<float>(bloadh(rzq, offq));
+              }
+              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+              rel[t] = dl >= D ? (qrh[t] + khi[kb]) : (dl <= -D ? (qrl[t] + klo[kb]) : band);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float p = fast_exp2(fmaf(s[qb][kb][t] + rel[t], sl2, -ql2[t]));
+            if (need_mask) {
+              const int i = i1 + t;
+              if (j >= N || (CAUSAL && j > i)) p = 0.f;
+            }
+            s[qb][kb][t] = p;
+            dp[qb][kb][t] = tau * p * (dp[qb][kb][t] - qdd[t]);
+          }
+        }
+      }
+
+      // key offset gradients and column sums
+      if (DZ || CS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int j = jw + 16 * kb + c16;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int i1 = i0 + 16 * qb + 4 * g;
+            const float gs = (dp[qb][kb][0] + dp[qb][kb][1]) + (dp[qb][kb][2] + dp[qb][kb][3]);
+            if (CS) csum[kb] += gs;
+            if (DZ) {
+              if (sat_lo) {
+                blo[kb] += gs;
+              } else if (sat_hi) {
+                bhi[kb] += gs;
+              } else {
+                float run[4];
+                bool any = false;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const int i = i1 + t;
+                  const int dl = i - j;
+                  const float gg = dp[qb][kb][t];
+                  float bandv = 0.f;
+                  if (dl >= D)
+                    bhi[kb] += gg;
+                  else if (dl <= -D)
+                    blo[kb] += gg;
+                  else {
+                    bandv = gg;
+                    any = any || (i < N && j < N && (!CAUSAL || j <= i));
+                  }
+                  run[t] = bandv;  // ascending columns
+                }
+                if (any) {
+                  bf16* row = reinterpret_cast<bf16*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh +
+                              gik.base + static_cast<int64_t>(j - j0b) * gik.pitch;
+                  store4(row + ((i1 - j + D) - gik.slo + gik.pad), run);
+                }
+              }
+            }
+          }
+        }
+      }
+
+      // dV^T += dO^T P ; dK^T += Q^T G  (K axis: the tile's 32 queries, in the
+      // order 4g + e, 16 + 4g + e of the lanes' own values)
+      {
+        bf16x8 pf[2], pl[2], gf[2], gl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[e >> 2][kb][e & 3];
+            const float y = dp[e >> 2][kb][e & 3];
+            pf[kb][e] = static_cast<bf16>(x);
+            gf[kb][e] = static_cast<bf16>(y);
+            if (SPLIT) {
+              pl[kb][e] = static_cast<bf16>(x - static_cast<float>(pf[kb][e]));
+              gl[kb][e] = static_cast<bf16>(y - static_cast<float>(gf[kb][e]));
+            }
+          }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4 dlo = lds_tr4(Ds, kP, 4 * g, 16 * db, c16);
+          const bf16x4 dhi = lds_tr4(Ds, kP, 16 + 4 * g, 16 * db, c16);
+          const bf16x4 qlo = lds_tr4(Qs, kP, 4 * g, 16 * db, c16);
+          const bf16x4 qhi = lds_tr4(Qs, kP, 16 + 4 * g, 16 * db, c16);
+          bf16x8 dt8, qt8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dt8[e] = dlo[e];
+            dt8[e + 4] = dhi[e];
+            qt8[e] = qlo[e];
+            qt8[e + 4] = qhi[e];
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            dv[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt8, pf[kb], dv[kb][db], 0, 0, 0);
+            dk[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt8, gf[kb], dk[kb][db], 0, 0, 0);
+            if (SPLIT) {
+              dv[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt8, pl[kb], dv[kb][db], 0, 0, 0);
+              dk[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt8, gl[kb], dk[kb][db], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    if (it + 1 < nqt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int j = jw + 16 * kb + c16;
+    const float lo = wave_sum_g(blo[kb]);
+    const float hi = wave_sum_g(bhi[kb]);
+    const float cs = wave_sum_g(csum[kb]);
+    if (j >= N) continue;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      float dvv[4] = {dv[kb][db][0], dv[kb][db][1], dv[kb][db][2], dv[kb][db][3]};
+      store_out4(a.dv, (tok + j) * 64 + 16 * db + 4 * g, a.out_f32 != 0, dvv);
+      float dkv[4] = {dk[kb][db][0], dk[kb][db][1], dk[kb][db][2], dk[kb][db][3]};
+      store4(a.dkacc + (tok + j) * 64 + 16 * db + 4 * g, dkv);
+    }
+    if (g == 0) {
+      if (DZ) {
+        a.bndk[(tok + j) * 2 + 0] = lo;
+        a.bndk[(tok + j) * 2 + 1] = hi;
+      }
+      if (CS) a.colsum[tok + j] = cs;
+    }
+  }
+}
+
+template <int F>
+hipError_t launch_kf(const AttnArgs& a, int B, hipStream_t s) {
+  const int nkb = (a.N + 127) / 128;
+  const int total = nkb * B * a.H;
+  const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
+  hipLaunchKernelGGL((bwd_k_fast<F>), dim3(total), dim3(256), 0, s, a, nkb, total, xcd_map);
+  return hipGetLastError();
+}
+
+#define RP_KF_FLAGS(X)                                                                    \
+  X(0) X(F_ZQ) X(F_BT) X(F_ZQ | F_ZK | F_DZK) X(F_ZK | F_DZK) X(F_ZK | F_BT | F_DZK)     \
+  X(F_U) X(F_ZQ | F_U) X(F_BT | F_U) X(F_ZQ | F_ZK | F_DZK | F_U) X(F_ZK | F_DZK | F_U)   \
+  X(F_ZK | F_BT | F_DZK | F_U)
+
+template <int SPL>
+hipError_t dispatch_kf(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZK | F_U);
+  switch (f) {
+#define RP_CASE(X)                                   \
+  case X:                                            \
+    return launch_kf<(X) | SPL>(a, B, s);            \
+  case (X) | F_CAUSAL:                               \
+    return launch_kf<(X) | F_CAUSAL | SPL>(a, B, s);
+    RP_KF_FLAGS(RP_CASE)
+#undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_k_bf16(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  if (flags & F_SPLIT) return dispatch_kf<F_SPLIT>(flags, a, B, s);
+  return dispatch_kf<0>(flags, a, B, s);
+}
+
+}  // namespace relpos

@@ -1,0 +1,405 @@
+// Query-parallel backward pass for bf16 inputs ([RPA] Table 9 "Query-parallel
+// pass", Algorithm 2).  [RPA] = "Fast and Exact Relative-Position Attention
+// via Structure-Aware Kernels" (arXiv 2611.01182).
+//
+// A workgroup of 4 waves owns 128 queries (one projection group), 32 per
+// wave.  Key tiles of 64 keys (K, V row-major; per-key boundary entries)
+// stream through double-buffered LDS.  Per tile and wave the pass rebuilds
+// the scores exactly as the forward does (same relation terms, same
+// boundary-entry rule) and, from the saved logsumexp L and D = rowdot(dO, O)
+// ([RPA] §3.1 Eq. (3), App. B tile-locality lemma):
+//   S^T = K Q^T and dP^T = V dO^T on MFMA (A from LDS rows, B in registers),
+//   P = exp2(S tau log2 e - L log2 e), G = tau P (dP - D),
+//   dQ^T += K^T G^T on MFMA (K^T read with the transposing LDS read; G as
+//   bf16, or bf16 hi + lo under F_SPLIT).
+// Offset gradients ([RPA] §4.2): a band pair (|delta| < D) writes its G to
+// dZ~^Q[i, delta + D] -- one entry per (query, offset), a single writer,
+// written as aligned 4-entry runs; pairs with |delta| >= D add into two fp32
+// per-query boundary sums kept on chip ("Local Boundary Sums").  No atomics.
+#include "relation.hpp"
+#include "tiles.hpp"
+
+namespace relpos {
+
+namespace {
+
+constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
+
+template <int F>
+__global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int total, int xcd_map) {
+  constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
+  constexpr bool SPLIT = (F & F_SPLIT) != 0;
+  constexpr bool DZ = (F & F_DZQ) != 0;
+  constexpr bool KC = (F & (F_ZK | F_U)) != 0;
+  constexpr bool KC3 = (F & F_ZK) != 0;
+  using GT = typename DzType<bf16, (F & F_DZ32) != 0>::type;
+  __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kP];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kP];
+  __shared__ __attribute__((aligned(16))) float skc[2][3][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = a.N, D = a.D;
+
+  int item = static_cast<int>(blockIdx.x);
+  if (xcd_map) {
+    const int q8 = total / 8, r8 = total % 8;
+    const int x = item % 8, slot = item / 8;
+    item = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + slot;
+  }
+  const int BH = total / nqb;
+  int bh, qblk;
+  if (CAUSAL) {
+    qblk = nqb - 1 - item / BH;
+    bh = item % BH;
+  } else {
+    bh = item / nqb;
+    qblk = item % nqb;
+  }
+  const int h = bh % a.H;
+  const int64_t tok = static_cast<int64_t>(bh) * N;
+  const int i0 = qblk * 128;
+  const int iw = i0 + 32 * wave;
+  const float sl2 = a.scale_log2, tau = a.scale;
+  const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
+  const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
+  const Rsrc rdo = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + tok * 64, slice_bytes);
+  const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
+  const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
+
+  bf16x8 qf[2][2], df[2][2];
+  float rlo[2], rhi[2], l2[2], dd[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int i = iw + 16 * qb + c16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t off = static_cast<uint32_t>(i * 128 + 64 * c + 16 * g);
+      qf[qb][c] = __builtin_bit_cast(bf16x8, bload16(rq, off));
+      df[qb][c] = __builtin_bit_cast(bf16x8, bload16(rdo, off));
+    }
+    const bool ok = i < N;
+    rlo[qb] = ok ? a.rowlo[tok + i] : 0.f;
+    rhi[qb] = ok ? a.rowhi[tok + i] : 0.f;
+    l2[qb] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
+    dd[qb] = ok ? a.dvec[tok + i] : 0.f;
+  }
+  GroupInfo giq = {0, 0, 0, 0};
+  if ((F & F_ZQ) || DZ) giq = a.gq[i0 / kGroup];
+  Rsrc rzq = rq, rzk = rq, rbt = rq;
+  if (F & F_ZQ)
+    rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,
+                    static_cast<uint64_t>(a.zq_bh) * 2);
+  if (F & F_ZK)
+    rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
+                    static_cast<uint64_t>(a.zk_bh) * 2);
+  if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+  GT* dzbase = DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh + giq.base : nullptr;
+
+  const int ilast_b = imin(N - 1, i0 + 127);
+  const int nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
+  const int nkt_w = CAUSAL ? imin(nkt, (iw + 31) / 64 + 1) : nkt;
+  int n_hi = (iw - D - 63 >= 0) ? (iw - D - 63) / 64 + 1 : 0;
+  n_hi = imin(n_hi, nkt_w);
+  int t_lo = CAUSAL ? nkt_w : (iw + 31 + D + 63) / 64;
+  t_lo = imax(n_hi, imin(t_lo, nkt_w));
+
+  floatx4 dq[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dq[qb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float blo[2] = {0.f, 0.f}, bhi[2] = {0.f, 0.f};
+
+  const int kr = tid >> 3, kc8 = (tid & 7) * 8;
+  uint4 tk[2], tv[2];
+  float tkc[3] = {0.f, 0.f, 0.f};
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t off = static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2);
+      tk[u] = bload16(rk, off);
+      tv[u] = bload16(rv, off);
+    }
+    if (KC && tid < 64) {
+      const int j = j0 + tid;
+      const bool ok = j < N;
+      tkc[2] = ok ? a.keymid[tok + j] : 0.f;
+      if (KC3) {
+        tkc[0] = ok ? a.keylo[tok + j] : 0.f;
+        tkc[1] = ok ? a.keyhi[tok + j] : 0.f;
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<uint4*>(&sk[buf][(kr + 32 * u) * kP + kc8]) = tk[u];
+      *reinterpret_cast<uint4*>(&sv[buf][(kr + 32 * u) * kP + kc8]) = tv[u];
+    }
+    if (KC && tid < 64) {
+      skc[buf][2][tid] = tkc[2];
+      if (KC3) {
+        skc[buf][0][tid] = tkc[0];
+        skc[buf][1][tid] = tkc[1];
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const int j0 = kt * 64;
+    if (kt + 1 < nkt) load_tile(j0 + 64);
+
+    if (kt < nkt_w) {
+      const bf16* Ks = sk[buf];
+      const bf16* Vs = sv[buf];
+      floatx4 s[2][4], dp[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kP + 32 * c + 8 * g);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (16 * kb + c16) * kP + 32 * c + 8 * g);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+            dp[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[qb][c], dp[qb][kb], 0, 0, 0);
+          }
+        }
+      }
+
+      // relation terms (same values as the forward); off = the row's
+      // constant on saturated tiles
+      const bool sat = kt < n_hi || kt >= t_lo;
+      const int side = kt < n_hi ? 1 : 0;
+      float off[2];
+      if (sat) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) off[qb] = side ? rhi[qb] : rlo[qb];
+        if (KC) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const floatx4 kx =
+                *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) s[qb][kb] += kx;
+          }
+        }
+      } else {
+        GroupInfo gik = {0, 0, 0, 0};
+        const int gk0 = (j0 / kGroup) * kGroup;
+        if (F & F_ZK) gik = a.gk[j0 / kGroup];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          off[qb] = 0.f;
+          const int i = iw + 16 * qb + c16;
+          const bool iok = i < N;
+          const int zrow = giq.base + (i - i0) * giq.pitch;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int j1 = j0 + 16 * kb + 4 * g;
+            float zq[4] = {0.f, 0.f, 0.f, 0.f};
+            if (F & F_ZQ) {
+              const int c0 = clamp_run((i - (j1 + 3) + D) - giq.slo + giq.pad, giq.pitch);
+              const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+              const halfx4 hv = __builtin_bit_cast(halfx4, w);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);
+            }
+            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int j = j1 + t;
+              const int dl = i - j;
+              const int jj = j - j0;
+              const float kedge = KC3 ? skc[buf][dl >= D ? 1 : 0][jj] : km[t];
+              float band = km[t] + zq[t];
+              if (F & F_ZK) {
+                const int cc = iclamp((dl + D) - gik.slo + gik.pad, 0, gik.pitch - 1);
+                const uint32_t offk =
+                    j < N ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + cc) * 2) : kOob;
+                band += static_cast<float>(bloadh(rzk, offk));
+              }
+              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            }
+          }
+        }
+      }
+      const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw);
+
+      // P and G = tau P (dP - D), in place of s
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int i = iw + 16 * qb + c16;
+        const float bias = off[qb] * sl2 - l2[qb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float p = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
+            if (need_mask) {
+              const int j = j0 + 16 * kb + 4 * g + t;
+              if (j >= N || (CAUSAL && j > i)) p = 0.f;
+            }
+            s[qb][kb][t] = tau * p * (dp[qb][kb][t] - dd[qb]);
+          }
+      }
+
+      // offset gradients of the queries
+      if (DZ) {
+        if (sat) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            float acc = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+              acc += (s[qb][kb][0] + s[qb][kb][1]) + (s[qb][kb][2] + s[qb][kb][3]);
+            if (side)
+              bhi[qb] += acc;
+            else
+              blo[qb] += acc;
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int i = iw + 16 * qb + c16;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const int j1 = j0 + 16 * kb + 4 * g;
+              float run[4];
+              bool any = false;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int j = j1 + t;
+                const int dl = i - j;
+                const float gg = s[qb][kb][t];
+                float bandv = 0.f;
+                if (dl >= D)
+                  bhi[qb] += gg;
+                else if (dl <= -D)
+                  blo[qb] += gg;
+                else {
+                  bandv = gg;
+                  any = any || (i < N && j < N && (!CAUSAL || j <= i));
+                }
+                run[3 - t] = bandv;  // descending columns
+              }
+              if (any) {
+                GT* row = dzbase + static_cast<int64_t>(i - i0) * giq.pitch;
+                store4(row + ((i - (j1 + 3) + D) - giq.slo + giq.pad), run);
+              }
+            }
+          }
+        }
+      }
+
+      // dQ^T += K^T G^T
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 gf[2], gl[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[qb][2 * c + (e >> 2)][e & 3];
+            gf[qb][e] = static_cast<bf16>(x);
+            if (SPLIT) gl[qb][e] = static_cast<bf16>(x - static_cast<float>(gf[qb][e]));
+          }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4 lo = lds_tr4(Ks, kP, 32 * c + 4 * g, 16 * db, c16);
+          const bf16x4 hi = lds_tr4(Ks, kP, 32 * c + 16 + 4 * g, 16 * db, c16);
+          bf16x8 kt8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kt8[e] = lo[e];
+            kt8[e + 4] = hi[e];
+          }
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            dq[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gf[qb], dq[qb][db], 0, 0, 0);
+            if (SPLIT)
+              dq[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gl[qb], dq[qb][db], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (kt + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int i = iw + 16 * qb + c16;
+    const float lo = wave_sum_g(blo[qb]);
+    const float hi = wave_sum_g(bhi[qb]);
+    if (i >= N) continue;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      float vals[4] = {dq[qb][db][0], dq[qb][db][1], dq[qb][db][2], dq[qb][db][3]};
+      store4(a.dqacc + (tok + i) * 64 + 16 * db + 4 * g, vals);
+    }
+    if (DZ && g == 0) {
+      a.bndq[(tok + i) * 2 + 0] = lo;
+      a.bndq[(tok + i) * 2 + 1] = hi;
+    }
+  }
+}
+
+template <int F>
+hipError_t launch_qf(const AttnArgs& a, int B, hipStream_t s) {
+  const int nqb = (a.N + 127) / 128;
+  const int total = nqb * B * a.H;
+  const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
+  hipLaunchKernelGGL((bwd_q_fast<F>), dim3(total), dim3(256), 0, s, a, nqb, total, xcd_map);
+  return hipGetLastError();
+}
+
+// term combinations: Shaw (ZQ), T5 (BT), DeBERTa (ZQ+ZK), Transformer-XL
+// (ZQ+U), and the other mixes of the descriptor's terms
+#define RP_QF_FLAGS(X)                                                                    \
+  X(0) X(F_U) X(F_ZK) X(F_ZK | F_U) X(F_ZQ | F_DZQ) X(F_ZQ | F_ZK | F_DZQ)               \
+  X(F_ZQ | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_DZQ | F_DZ32) X(F_ZQ | F_U | F_DZQ)         \
+  X(F_ZQ | F_U | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_U | F_DZQ) X(F_ZQ | F_ZK | F_U | F_DZQ | F_DZ32) \
+  X(F_BT | F_DZQ | F_DZ32) X(F_BT | F_U | F_DZQ | F_DZ32) X(F_ZK | F_BT | F_DZQ | F_DZ32)  \
+  X(F_ZK | F_BT | F_U | F_DZQ | F_DZ32)
+
+template <int SPL>
+hipError_t dispatch_qf(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  const int f = flags & (F_ZQ | F_ZK | F_BT | F_U | F_CAUSAL | F_DZQ | F_DZ32);
+  switch (f) {
+#define RP_CASE(X)                                   \
+  case X:                                            \
+    return launch_qf<(X) | SPL>(a, B, s);            \
+  case (X) | F_CAUSAL:                               \
+    return launch_qf<(X) | F_CAUSAL | SPL>(a, B, s);
+    RP_QF_FLAGS(RP_CASE)
+#undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  if (flags & F_SPLIT) return dispatch_qf<F_SPLIT>(flags, a, B, s);
+  return dispatch_qf<0>(flags, a, B, s);
+}
+
+}  // namespace relpos

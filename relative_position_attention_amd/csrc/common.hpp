@@ -147,16 +147,42 @@ __device__ __forceinline__ void load4_guard(const float* p, int idx, int n, floa
   }
 }
 
-__device__ __forceinline__ float wave_max_g(float v) {
-  // reduce over the four lane groups l>>4 that share l&15
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Reductions over the four lane groups l>>4 that share l&15, with the gfx950
+// lane-swap instructions: permlane16_swap pairs every lane with lane l^16 and
+// permlane32_swap with l^32 (each returns the pair of values, in an order
+// that depends on the lane, so the symmetric max / sum of the two is taken).
+__device__ __forceinline__ float xor16_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum_g(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float xor32_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max_g(float v) { return xor32_pair_max(xor16_pair_max(v)); }
+// (the two operands of each add are the same pair in both lanes, so all four
+// lanes of a column get bitwise the same sum)
+__device__ __forceinline__ float wave_sum_g(float v) { return xor32_pair_sum(xor16_pair_sum(v)); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// m receives tile[row0 + e][col0 + m] for e = 0..3 from a row-major bf16 tile
+// of pitch `pitch`: the instruction hands lane m element m%4 of the 8-byte
+// blocks addressed by lanes m/4 + 4e, so lane r addresses row row0 + r/4,
+// columns col0 + 4 (r%4) .. +3.  row0 may differ between the four groups.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* tile, int pitch, int row0, int col0, int m) {
+  const bf16* p = tile + (row0 + (m >> 2)) * pitch + col0 + 4 * (m & 3);
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

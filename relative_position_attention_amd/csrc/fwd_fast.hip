@@ -6,8 +6,9 @@
 // projection group); each wave owns 32 of them (two 16-query blocks), which
 // keeps a wave within 128 registers so four workgroups share a CU and the
 // MFMA work of some waves overlaps the softmax of others.  Key tiles of 64
-// keys stream through LDS, double buffered: K row-major, V transposed, and
-// (when a per-key relation term exists) the tile's per-key boundary entries.
+// keys stream through LDS, double buffered: K and V row-major (the V^T
+// operand of P V is read with the gfx950 transposing LDS read), and (when a
+// per-key relation term exists) the tile's per-key boundary entries.
 // All global reads are buffer loads: 32-bit offsets, and reads past a slice
 // return zero, so no lane branches on bounds.  Per tile and wave:
 //   S^T = K Q^T on 16x16x32 bf16 MFMA (each lane owns one query column and
@@ -37,13 +38,8 @@ namespace {
 constexpr int QB = 2;              // 16-query blocks per wave
 constexpr int kWQ = 16 * QB;       // queries per wave
 constexpr int kBM = 4 * kWQ;       // queries per workgroup
-constexpr int kKP = 72;            // K tile pitch (bf16): 144-byte rows
-constexpr int kVP = 68;            // V^T tile pitch (bf16): 136-byte rows
+constexpr int kKP = 72;            // K and V tile pitch (bf16): 144-byte rows
 constexpr float kLazy = 8.f;       // rescale threshold, log2 units
-
-__device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
 
 template <int F>
 __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
@@ -56,7 +52,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
-  __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kVP];
+  __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kKP];
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
 
   const int tid = threadIdx.x;
@@ -138,17 +134,15 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
     for (int db = 0; db < 4; ++db) o[qb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // tile staging: K rows (t>>3) and 32 + (t>>3), chunk t&7; V rows 2(t&31),
-  // 2(t&31)+1, chunk t>>5 (written transposed as bf16 pairs)
+  // tile staging: K and V rows (t>>3) and 32 + (t>>3), chunk t&7
   const int kr = tid >> 3, kc8 = (tid & 7) * 8;
-  const int vr = (tid & 31) * 2, vc8 = (tid >> 5) * 8;
   uint4 tk[2], tv[2];
   float tkc[3] = {0.f, 0.f, 0.f};
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       tk[u] = bload16(rk, static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2));
-      tv[u] = bload16(rv, static_cast<uint32_t>((j0 + vr + u) * 128 + vc8 * 2));
+      tv[u] = bload16(rv, static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2));
     }
     if (KC && tid < 64) {
       const int j = j0 + tid;
@@ -162,15 +156,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
       *reinterpret_cast<uint4*>(&sk[buf][(kr + 32 * u) * kKP + kc8]) = tk[u];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // element e of rows vr and vr + 1 as one bf16 pair
-      const uint32_t w0 = word4(tv[0], e >> 1), w1 = word4(tv[1], e >> 1);
-      const uint32_t pair = (e & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
-                                    : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&sv[buf][(vc8 + e) * kVP + vr]) = pair;
+      *reinterpret_cast<uint4*>(&sv[buf][(kr + 32 * u) * kKP + kc8]) = tv[u];
     }
     if (KC && tid < 64) {
       skc[buf][2][tid] = tkc[2];
@@ -192,7 +180,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
 
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
-      const bf16* Vt = sv[buf];
+      const bf16* Vs = sv[buf];
       floatx4 s[QB][4];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -329,9 +317,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16* row = Vt + (16 * db + c16) * kVP + 32 * c + 4 * g;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16);
+          // V^T rows 16 db + c16, keys 32 c + 4 g + (0..3) and + 16
+          const bf16x4 lo = lds_tr4(Vs, kKP, 32 * c + 4 * g, 16 * db, c16);
+          const bf16x4 hi = lds_tr4(Vs, kKP, 32 * c + 16 + 4 * g, 16 * db, c16);
           bf16x8 vf;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {

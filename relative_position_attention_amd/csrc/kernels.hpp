@@ -64,6 +64,10 @@ hipError_t launch_attn_fwd(int dtype, int flags, const AttnArgs& a, int B, hipSt
 hipError_t launch_attn_fwd_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_bwd_q(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_bwd_k(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+// bf16 backward passes: 32 tokens per wave, buffer loads, transposing LDS
+// reads (bwd_q_fast.hip, bwd_k_fast.hip)
+hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_k_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
 
 // ---- auxiliary kernels (aux.hip)
 
@@ -169,6 +173,8 @@ struct FinalizeArgs {
   int dz_f32;  // entries are fp32
 };
 hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s);
+// bf16: aligned 16-byte staging of the offset gradients (reduce_fast.hip)
+hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s);
 
 // Table-gradient partials per (head, token chunk) ([RPA] "Deterministic table
 // gradients", first kernel): P1[h][c][s][:] = sum_i dZ~[i,s] x_i,
@@ -185,6 +191,7 @@ struct PartialArgs {
   int dz_f32;     // entries are fp32 (scalar bias without a query table)
 };
 hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s);
+hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s);
 
 // Second kernel: fixed-order sums over chunks (and heads of a shared table),
 // then the bucket fold dA[r] = sum over copies s of r ([RPA] App. B.1
@@ -200,29 +207,35 @@ struct FoldArgs {
 };
 hipError_t launch_fold_table(int dtype, const FoldArgs& f, hipStream_t s);
 
+// db[h][s] = sum over chunks of P2 (fixed order)
+hipError_t launch_p2_sum(const float* p2, float* db, int H, int S, int nchunk, hipStream_t s);
+
+// dbias[r, h] = sum over the copies of row r of db[h][s] (bucket fold)
 struct FoldBiasArgs {
-  const float* p2;
-  const int32_t* fold;
+  const float* db;      // [H, S]
+  const int32_t* fold;  // [R, 2] intervals
   float* out;
   int64_t row_stride, head_stride;
-  int H, R, S, nchunk;
+  int H, R, S;
 };
 hipError_t launch_fold_bias(const FoldBiasArgs& f, hipStream_t s);
 
-// dv[h] = sum_s (sum_c P2[h][c][s]) A~^Q[s]
+// dv[h] = sum_s db[h][s] A~^Q[s], two phases through part [H, 64, 64]
 struct DvArgs {
-  const float* p2;
+  const float* db;
   const void* atq;
   int at_shared;
+  float* part;
   float* out;
-  int H, S, nchunk;
+  int H, S;
 };
 hipError_t launch_dv(int dtype, const DvArgs& a, hipStream_t s);
 
-// du[h] = sum_{b,j} colsum[b,h,j] k[b,h,j]
+// du[h] = sum_{b,j} colsum[b,h,j] k[b,h,j], two phases through part
 struct DuArgs {
   const float* colsum;
   const void* k;
+  float* part;
   float* out;
   int B, H, N;
 };

@@ -486,6 +486,10 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     off = align256(off + static_cast<size_t>(p.H) * p.nchunk * p.S * kHeadDim * 4);
   p.ws_p2 = off;
   off = align256(off + static_cast<size_t>(p.H) * p.nchunk * p.S * 4);
+  p.ws_db = off;  // [H, S] chunk-summed P2
+  off = align256(off + static_cast<size_t>(p.H) * p.S * 4);
+  p.ws_red = off;  // [H, 64, 64] two-phase row-sum partials (dv, du)
+  off = align256(off + static_cast<size_t>(p.H) * 64 * 64 * 4);
   p.ws_bwd_end = off;
   return RELPOS_OK;
 }

@@ -55,7 +55,7 @@ struct Plan {
          ws_atq = 0, ws_atk = 0, ws_fwd_end = 0;
   // ---- byte offsets inside ws (backward part, after ws_fwd_end) ----
   size_t ws_D = 0, ws_dqacc = 0, ws_dkacc = 0, ws_dz = 0, ws_bndq = 0, ws_bndk = 0,
-         ws_colsum = 0, ws_p1 = 0, ws_p2 = 0, ws_bwd_end = 0;
+         ws_colsum = 0, ws_p1 = 0, ws_p2 = 0, ws_db = 0, ws_red = 0, ws_bwd_end = 0;
 };
 
 // Builds the plan; returns RELPOS_OK or an error code with `detail` set.

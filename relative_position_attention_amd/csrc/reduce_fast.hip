@@ -1,0 +1,350 @@
+// Reductions of the offset gradients for bf16 inputs ([RPA] Table 9 "Query
+// reduction" / "Key reduction"; [RPA] §4.2 and the table-gradient lemma of
+// App. B.1).  [RPA] = "Fast and Exact Relative-Position Attention via
+// Structure-Aware Kernels" (arXiv 2611.01182).
+//
+// The offset gradients dZ~[i, s] sit in the skewed per-group rows of the
+// projection layout: row i of group g holds expanded rows s in [slo_g, shi_g]
+// at column s - slo_g + pad_g.  Both kernels stage (64 tokens x 64 rows s)
+// tiles of it into LDS with aligned 16-byte loads (each token row's segment
+// is contiguous; entries a token cannot reach, and the two boundary rows, are
+// written as zero) and run the products on MFMA:
+//   finalize_fast:  out = acc + dZ~ A~ (band rows) + the two boundary sums
+//                   times A~[0], A~[2D] in fp32 (+ column sums times u);
+//                   dQ = tau dS K + dZ^Q A^Q of the table-gradient lemma, the
+//                   bucket fold implicit (copies multiply the same row);
+//   partials_fast:  P1[h][c][s] = sum over the tokens of chunk c of
+//                   dZ~[i, s] x_i and P2[h][c][s] = sum of dZ~[i, s]: the
+//                   fixed-order chunk partials of [RPA] "Deterministic table
+//                   gradients" (the chunk sums and the fold follow).
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace relpos {
+
+namespace {
+
+constexpr int kRP = 72;   // LDS pitch of bf16 tiles (144-byte rows)
+constexpr int kFP = 68;   // LDS pitch of fp32 tiles
+
+// Stage dZ~ for tokens r0 .. r0+63 (one group) and expanded rows s0 .. s0+63
+// into zt (bf16, [token][s]) and optionally zf (fp32).  Entries outside the
+// token's reachable band rows [max(smin, 1), min(smax, 2D-1)] are zero.
+template <typename GT, bool F32COPY>
+__device__ __forceinline__ void stage_dz(const Rsrc& rz, const GroupInfo& gi, int g0, int r0,
+                                         int s0, int N, int D, bool key_side, bool causal,
+                                         bf16* zt, float* zf) {
+  constexpr int VEC = 16 / sizeof(GT);
+  constexpr int NCH = 64 / VEC + 1;  // aligned chunks covering 64 entries
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, tq = tid & 3;
+  const int i = r0 + r;
+  int smin = 1, smax = 0;
+  if (i < N) {
+    if (key_side)
+      key_s_range(i, N, D, causal, smin, smax);
+    else
+      query_s_range(i, N, D, causal, smin, smax);
+  }
+  smin = imax(smin, 1);
+  smax = imin(smax, 2 * D - 1);
+  const int rowbase = gi.base + (i - g0) * gi.pitch;          // element offset of column 0
+  const int e0 = rowbase + (s0 - gi.slo + gi.pad);            // element of s0
+  const int c_first = e0 & ~(VEC - 1);
+  for (int ch = tq; ch < NCH; ch += 4) {
+    const int ce = c_first + ch * VEC;
+    if (ce > e0 + 63) break;
+    const uint4 w = bload16(rz, ce >= 0 ? static_cast<uint32_t>(ce) * sizeof(GT) : kOob);
+    GT vals[VEC];
+    __builtin_memcpy(vals, &w, 16);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int s = s0 + (ce + e - e0);
+      if (s < s0 || s > s0 + 63) continue;
+      const float v = (i < N && s >= smin && s <= smax) ? to_f(vals[e]) : 0.f;
+      zt[r * kRP + (s - s0)] = static_cast<bf16>(v);
+      if (F32COPY) zf[r * kFP + (s - s0)] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- finalize
+
+template <typename GT>
+__global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
+  __shared__ __attribute__((aligned(16))) bf16 zt[64 * kRP];
+  __shared__ __attribute__((aligned(16))) bf16 at[64 * kRP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int bh = blockIdx.y;
+  const int h = bh % f.H;
+  const int r0 = blockIdx.x * 64;
+  const int64_t tok = static_cast<int64_t>(bh) * f.N;
+  const int D = f.D;
+  floatx4 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bf16* atab = nullptr;
+  if (f.at != nullptr)
+    atab = reinterpret_cast<const bf16*>(f.at) + static_cast<int64_t>(f.at_shared ? 0 : h) * f.S * 64;
+
+  if (f.dz != nullptr && D >= 1) {
+    const int grp = r0 / kGroup;
+    const GroupInfo gi = f.gi[grp];
+    int slo, shi;
+    if (f.key_side)
+      key_group_window(grp, f.N, D, f.causal != 0, slo, shi);
+    else
+      query_group_window(grp, f.N, D, f.causal != 0, slo, shi);
+    const int sa = imax(1, slo), sb = imin(2 * D - 1, shi);
+    const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(f.dz) + static_cast<int64_t>(bh) * f.dz_bh,
+                              static_cast<uint64_t>(f.dz_bh) * sizeof(GT));
+    const Rsrc ra = make_rsrc(atab, static_cast<uint64_t>(f.S) * 128);
+    for (int s0 = sa; s0 <= sb; s0 += 64) {
+      stage_dz<GT, false>(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0, zt,
+                          nullptr);
+      {
+        // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
+        const int ar = tid >> 2, ac = (tid & 3) * 16;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint4 w = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
+          *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = w;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
+        const bf16* zr = zt + (16 * wave + c16) * kRP + 32 * c + 4 * g;
+        const bf16x4 zlo = *reinterpret_cast<const bf16x4*>(zr);
+        const bf16x4 zhi = *reinterpret_cast<const bf16x4*>(zr + 16);
+        bf16x8 a8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a8[e] = zlo[e];
+          a8[e + 4] = zhi[e];
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4 blo = lds_tr4(at, kRP, 32 * c + 4 * g, 16 * db, c16);
+          const bf16x4 bhi = lds_tr4(at, kRP, 32 * c + 16 + 4 * g, 16 * db, c16);
+          bf16x8 b8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            b8[e] = blo[e];
+            b8[e + 4] = bhi[e];
+          }
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[db], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds rows 16 wave + 4g + t, column 16 db + c16
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = r0 + 16 * wave + 4 * g + t;
+    if (i >= f.N) continue;
+    const int64_t row = tok + i;
+    float b0 = 0.f, b1 = 0.f, cs = 0.f;
+    if (atab != nullptr && f.bnd != nullptr) {
+      b0 = f.bnd[row * 2 + 0];
+      b1 = f.bnd[row * 2 + 1];
+    }
+    if (f.colsum != nullptr) cs = f.colsum[row];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d = 16 * db + c16;
+      float v = acc[db][t] + f.acc[row * 64 + d];
+      if (atab != nullptr)
+        v += b0 * static_cast<float>(atab[d]) + b1 * static_cast<float>(atab[static_cast<int64_t>(2 * D) * 64 + d]);
+      if (f.colsum != nullptr) v += cs * static_cast<float>(reinterpret_cast<const bf16*>(f.u)[h * 64 + d]);
+      if (f.out_f32)
+        reinterpret_cast<float*>(f.out)[row * 64 + d] = v;
+      else
+        reinterpret_cast<bf16*>(f.out)[row * 64 + d] = static_cast<bf16>(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- partials
+
+template <typename GT>
+__global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16 zt[64 * kRP];  // [token][s]
+  __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];  // [token][d]
+  __shared__ __attribute__((aligned(16))) float zf[64 * kFP]; // fp32 copy for the plain sums
+  __shared__ float bsh[2][64];
+  __shared__ float p2red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int s0 = blockIdx.x * 64;
+  const int h = blockIdx.y;
+  const int chunk = blockIdx.z;
+  const int D = p.D;
+  const int nrb = (p.N + 63) / 64;
+  const int total = p.B * nrb;
+  const int per = (total + p.nchunk - 1) / p.nchunk;
+  const int sb0 = chunk * per, sb1 = imin(total, sb0 + per);
+  const bool has0 = s0 == 0;
+  const bool has2 = (2 * D >= s0) && (2 * D < s0 + 64);
+  const bool want_p1 = p.p1 != nullptr;
+  const bool want_p2 = p.p2 != nullptr;
+
+  floatx4 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float p2acc = 0.f;           // thread (s = tid & 63, quarter tid >> 6)
+  float bx0 = 0.f, bx1 = 0.f;  // boundary P1 (threads < 64: d = tid)
+  float bs0 = 0.f, bs1 = 0.f;  // boundary P2 (every thread < 64, same order)
+
+  for (int sb = sb0; sb < sb1; ++sb) {
+    const int b = sb / nrb, rb = sb % nrb;
+    const int r0 = rb * 64;
+    const int grp = r0 / kGroup;
+    int slo, shi;
+    if (p.key_side)
+      key_group_window(grp, p.N, D, p.causal != 0, slo, shi);
+    else
+      query_group_window(grp, p.N, D, p.causal != 0, slo, shi);
+    const int sa = imax(1, slo), se = imin(2 * D - 1, shi);
+    const bool band_hit = D >= 1 && sa <= se && s0 <= se && s0 + 63 >= sa;
+    if (!band_hit && !has0 && !has2) continue;  // uniform
+    const int64_t bhs = static_cast<int64_t>(b) * p.H + h;
+    const int64_t tok = bhs * p.N;
+    if (want_p1) {
+      const Rsrc rx = make_rsrc(reinterpret_cast<const bf16*>(p.x) + tok * 64,
+                                static_cast<uint64_t>(p.N) * 128);
+      const int xr = tid >> 2, xc = (tid & 3) * 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 w = bload16(rx, static_cast<uint32_t>((r0 + xr) * 128 + (xc + 8 * u) * 2));
+        *reinterpret_cast<uint4*>(&xt[xr * kRP + xc + 8 * u]) = w;
+      }
+    }
+    if (band_hit) {
+      const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(p.dz) + bhs * p.dz_bh,
+                                static_cast<uint64_t>(p.dz_bh) * sizeof(GT));
+      stage_dz<GT, true>(rz, p.gi[grp], grp * kGroup, r0, s0, p.N, D, p.key_side != 0,
+                         p.causal != 0, zt, zf);
+    }
+    if (has0 || has2) {
+      if (tid < 64) {
+        const int i = r0 + tid;
+        bsh[0][tid] = i < p.N ? p.bnd[(tok + i) * 2 + 0] : 0.f;
+        bsh[1][tid] = i < p.N ? p.bnd[(tok + i) * 2 + 1] : 0.f;
+      }
+    }
+    __syncthreads();
+    if (band_hit) {
+      if (want_p1) {
+        // P1 (s x d) += Z^T (s x tokens) X (tokens x d); K axis (tokens) in
+        // the order 32c + 4g + e, 32c + 16 + 4g + e
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x4 alo = lds_tr4(zt, kRP, 32 * c + 4 * g, 16 * wave, c16);
+          const bf16x4 ahi = lds_tr4(zt, kRP, 32 * c + 16 + 4 * g, 16 * wave, c16);
+          bf16x8 a8;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a8[e] = alo[e];
+            a8[e + 4] = ahi[e];
+          }
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x4 blo = lds_tr4(xt, kRP, 32 * c + 4 * g, 16 * db, c16);
+            const bf16x4 bhi = lds_tr4(xt, kRP, 32 * c + 16 + 4 * g, 16 * db, c16);
+            bf16x8 b8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              b8[e] = blo[e];
+              b8[e + 4] = bhi[e];
+            }
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[db], 0, 0, 0);
+          }
+        }
+      }
+      if (want_p2) {
+        // column s = tid & 63, tokens 16 (tid >> 6) .. +15, in order
+        const int s = tid & 63, q = tid >> 6;
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part += zf[(16 * q + e) * kFP + s];
+        p2acc += part;
+      }
+    }
+    if (has0 || has2) {
+      if (want_p1 && tid < 64) {
+        for (int tk = 0; tk < 64; ++tk) {
+          const float xv = static_cast<float>(xt[tk * kRP + tid]);
+          bx0 += bsh[0][tk] * xv;
+          bx1 += bsh[1][tk] * xv;
+        }
+      }
+      if (want_p2 && tid < 64) {
+        // every writer thread of P2 holds the boundary sums (the row s = 2D
+        // is written by thread 2D - s0)
+        for (int tk = 0; tk < 64; ++tk) {
+          bs0 += bsh[0][tk];
+          bs1 += bsh[1][tk];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // write the chunk's partials
+  const int64_t pbase = (static_cast<int64_t>(h) * p.nchunk + chunk) * p.S;
+  if (want_p1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int s = s0 + 16 * wave + 4 * g + t;
+      if (s >= p.S) continue;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) p.p1[(pbase + s) * 64 + 16 * db + c16] = acc[db][t];
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // boundary rows: added in a fixed order after the band part
+      if (has0) p.p1[(pbase + 0) * 64 + tid] += bx0 + (2 * D == 0 ? bx1 : 0.f);
+      if (has2 && D > 0) p.p1[(pbase + 2 * D) * 64 + tid] += bx1;
+    }
+  }
+  if (want_p2) {
+    p2red[tid >> 6][tid & 63] = p2acc;
+    __syncthreads();
+    if (tid < 64) {
+      const int s = s0 + tid;
+      if (s < p.S) {
+        float v = ((p2red[0][tid] + p2red[1][tid]) + p2red[2][tid]) + p2red[3][tid];
+        if (has0 && s == 0) v += bs0 + (2 * D == 0 ? bs1 : 0.f);
+        if (has2 && D > 0 && s == 2 * D) v += bs1;
+        p.p2[pbase + s] = v;
+      }
+    }
+  }
+}
+
+inline unsigned nblk(int64_t n, int b) { return static_cast<unsigned>((n + b - 1) / b); }
+
+}  // namespace
+
+hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s) {
+  dim3 grid(nblk(f.N, 64), BH);
+  if (f.dz_f32)
+    hipLaunchKernelGGL((finalize_fast<float>), grid, dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL((finalize_fast<bf16>), grid, dim3(256), 0, s, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s) {
+  dim3 grid(nblk(p.S, 64), p.H, p.nchunk);
+  if (p.dz_f32)
+    hipLaunchKernelGGL((partials_fast<float>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((partials_fast<bf16>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace relpos
