@@ -35,6 +35,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
+  // query projections of a band tile are staged into LDS once per workgroup
+  constexpr bool STZQ = (F & F_ZQ) != 0;
+  constexpr int kZP = 136;  // szq pitch (fp16)
+  __shared__ __attribute__((aligned(16))) _Float16 szq[STZQ ? kT * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sq[2][kT * kP];
   __shared__ __attribute__((aligned(16))) bf16 sd[2][kT * kP];
   __shared__ __attribute__((aligned(16))) float sqs[2][4][kT];  // l2, D, rowlo, rowhi
@@ -155,6 +159,34 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     const int buf = (it - it0) & 1;
     const int i0 = it * kT;
     if (it + 1 < nqt) load_tile(i0 + kT);
+    if (STZQ) {
+      // band for some wave of the workgroup: stage Z^Q of the tile's queries
+      // for the workgroup's 128 keys, as szq[query][key - j0b]; a query row
+      // holds them as 128 consecutive entries in descending key order from a
+      // 16-byte boundary (the query-side pad), so each chunk is reversed
+      const bool blk_sat = (i0 - (j0b + 127) >= D) || (i0 + kT - 1 - j0b <= -D);
+      if (!blk_sat) {
+        const GroupInfo gq = a.gq[i0 / kGroup];
+        const int gq0s = (i0 / kGroup) * kGroup;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int idx = tid + 256 * u;
+          const int r = idx >> 4, ch = idx & 15;
+          const int i = i0 + r;
+          const int col = (i - (j0b + 127) + D) - gq.slo + gq.pad + 8 * ch;
+          const int e = gq.base + (i - gq0s) * gq.pitch + col;
+          const uint4 w = bload16(rzq, (i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
+          // entries 8 ch .. 8 ch + 7 of the run are keys j0b + 127 - 8 ch - (0..7)
+          uint4 rev;
+          rev.x = __builtin_amdgcn_perm(w.w, w.w, 0x01000302u);
+          rev.y = __builtin_amdgcn_perm(w.z, w.z, 0x01000302u);
+          rev.z = __builtin_amdgcn_perm(w.y, w.y, 0x01000302u);
+          rev.w = __builtin_amdgcn_perm(w.x, w.x, 0x01000302u);
+          *reinterpret_cast<uint4*>(szq + r * kZP + (120 - 8 * ch)) = rev;
+        }
+        __syncthreads();
+      }
+    }
 
     if (it >= itw) {
       const bf16* Qs = sq[buf];
@@ -183,9 +215,6 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
       const bool sat_lo = it < n_lo, sat_hi = it >= t_hi;
       const bool need_mask = (i0 + kT > N) || (jw + 32 > N) || (CAUSAL && i0 < jw + 31);
-      GroupInfo giq = {0, 0, 0, 0};
-      if (F & F_ZQ) giq = a.gq[i0 / kGroup];
-      const int gq0 = (i0 / kGroup) * kGroup;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int i1 = i0 + 16 * qb + 4 * g;
@@ -211,17 +240,16 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 #pragma unroll
               for (int t = 0; t < 4; ++t) zk[t] = static_cast<float>(hv[t]);  // ascending
             }
+            halfx4 zq4 = halfx4{0, 0, 0, 0};
+            if (STZQ)  // Z^Q[i1 + t][i1 + t - j + D], t = 0..3
+              zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq), kZP,
+                                                       16 * qb + 4 * g, 32 * wave + 16 * kb, c16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i = i1 + t;
               const int dl = i - j;
               float band = kmid[kb] + zk[t];
-              if (F & F_ZQ) {
-                const int cc = iclamp((dl + D) - giq.slo + giq.pad, 0, giq.pitch - 1);
-                const uint32_t offq =
-                    i < N ? static_cast<uint32_t>((giq.base + (i - gq0) * giq.pitch + cc) * 2) : kOob;
-                band += static_cast<float>(bloadh(rzq, offq));
-              }
+              if (F & F_ZQ) band += static_cast<float>(zq4[t]);
               if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
               rel[t] = dl >= D ? (qrh[t] + khi[kb]) : (dl <= -D ? (qrl[t] + klo[kb]) : band);
             }

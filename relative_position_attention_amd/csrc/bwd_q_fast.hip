@@ -33,6 +33,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
   using GT = typename DzType<bf16, (F & F_DZ32) != 0>::type;
+  // key projections of a band tile are staged into LDS once per workgroup
+  constexpr bool STZK = (F & F_ZK) != 0;
+  constexpr int kZP = 136;  // szk pitch (fp16)
+  __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kP];
   __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kP];
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
@@ -154,6 +158,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     const int buf = kt & 1;
     const int j0 = kt * 64;
     if (kt + 1 < nkt) load_tile(j0 + 64);
+    if (STZK) {
+      // band for some wave of the workgroup: stage Z^K of the tile's keys
+      const bool blk_sat = (i0 - (j0 + 63) >= D) || (i0 + 127 - j0 <= -D);
+      if (!blk_sat && j0 < N) {
+        const GroupInfo gk = a.gk[j0 / kGroup];
+        stage_zk_rows(rzk, gk.base, gk.slo, gk.pad, gk.pitch, (j0 / kGroup) * kGroup, j0, i0, D,
+                      szk, kZP);
+        __syncthreads();
+      }
+    }
 
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
@@ -198,9 +212,6 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           }
         }
       } else {
-        GroupInfo gik = {0, 0, 0, 0};
-        const int gk0 = (j0 / kGroup) * kGroup;
-        if (F & F_ZK) gik = a.gk[j0 / kGroup];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           off[qb] = 0.f;
@@ -218,24 +229,28 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 #pragma unroll
               for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);
             }
-            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
             if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+            if (KC3) {
+              klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
+              khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
+            }
+            halfx4 zk4 = halfx4{0, 0, 0, 0};
+            if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
+              zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
+                                                       16 * kb + 4 * g, 32 * wave + 16 * qb, c16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int j = j1 + t;
               const int dl = i - j;
-              const int jj = j - j0;
-              const float kedge = KC3 ? skc[buf][dl >= D ? 1 : 0][jj] : km[t];
+              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
               float band = km[t] + zq[t];
-              if (F & F_ZK) {
-                const int cc = iclamp((dl + D) - gik.slo + gik.pad, 0, gik.pitch - 1);
-                const uint32_t offk =
-                    j < N ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + cc) * 2) : kOob;
-                band += static_cast<float>(bloadh(rzk, offk));
-              }
+              if (F & F_ZK) band += static_cast<float>(zk4[t]);
               if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
               s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
             }
+            // keep each 4-run's loads next to their use (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }

@@ -218,4 +218,25 @@ __device__ __forceinline__ void store_out4(void* base, int64_t idx, bool f32, co
     store4(reinterpret_cast<bf16*>(base) + idx, v);
 }
 
+// Stage the key-side projections Z^K of keys j0 .. j0+63 for queries
+// i0 .. i0+127 (one 128-query block) into szk[key][query] (fp16, pitch
+// `pitch`): key row j holds them as 128 consecutive entries (ascending in i)
+// starting on a 16-byte boundary (the key-side pad), so each thread moves four
+// aligned 16-byte chunks.  Rows past the slice read zero.
+__device__ __forceinline__ void stage_zk_rows(const Rsrc& rzk, int gbase, int gslo, int gpad,
+                                              int gpitch, int gk0, int j0, int i0, int D,
+                                              _Float16* szk, int pitch) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u;
+    const int r = idx >> 4, ch = idx & 15;
+    const int j = j0 + r;
+    const int col = (i0 - j + D) - gslo + gpad + 8 * ch;
+    const int e = gbase + (j - gk0) * gpitch + col;
+    const uint4 w = bload16(rzk, e >= 0 ? static_cast<uint32_t>(e) * 2 : kOob);
+    *reinterpret_cast<uint4*>(szk + r * pitch + 8 * ch) = w;
+  }
+}
+
 }  // namespace relpos

@@ -51,6 +51,10 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
   // they are one value u . k_j
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
+  // key projections of a band tile are staged into LDS once per workgroup
+  constexpr bool STZK = (F & F_ZK) != 0;
+  constexpr int kZP = 136;  // szk pitch (fp16)
+  __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
   __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kKP];
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
@@ -177,6 +181,16 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
     const int buf = kt & 1;
     const int j0 = kt * 64;
     if (kt + 1 < nkt) load_tile(j0 + 64);
+    if (STZK) {
+      // band for some wave of the workgroup: stage Z^K of the tile's keys
+      const bool blk_sat = (i0 - (j0 + 63) >= D) || (i0 + kBM - 1 - j0 <= -D);
+      if (!blk_sat && j0 < N) {
+        const GroupInfo gk = a.gk[j0 / kGroup];
+        stage_zk_rows(rzk, gk.base, gk.slo, gk.pad, gk.pitch, (j0 / kGroup) * kGroup, j0, i0, D,
+                      szk, kZP);
+        __syncthreads();
+      }
+    }
 
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
@@ -216,9 +230,6 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
       } else {
         // band tile: per-pair terms; pairs with |delta| >= D take the
         // boundary entries
-        GroupInfo gik = {0, 0, 0, 0};
-        const int gk0 = (j0 / kGroup) * kGroup;
-        if (F & F_ZK) gik = a.gk[j0 / kGroup];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           off[qb] = 0.f;
@@ -236,22 +247,24 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int
 #pragma unroll
               for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);  // descending
             }
-            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
             if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+            if (KC3) {
+              klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
+              khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
+            }
+            halfx4 zk4 = halfx4{0, 0, 0, 0};
+            if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
+              zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
+                                                       16 * kb + 4 * g, kWQ * wave + 16 * qb, c16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int j = j1 + t;
               const int dl = i - j;
-              const int jj = j - j0;
-              // boundary pairs: the row's entry plus the key's (one LDS read)
-              const float kedge = KC3 ? skc[buf][dl >= D ? 1 : 0][jj] : km[t];
+              // boundary pairs: the row's entry plus the key's
+              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
               float band = km[t] + zq[t];
-              if (F & F_ZK) {
-                const int cc = iclamp((dl + D) - gik.slo + gik.pad, 0, gik.pitch - 1);
-                const uint32_t offk =
-                    j < N ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + cc) * 2) : kOob;
-                band += static_cast<float>(bloadh(rzk, offk));
-              }
+              if (F & F_ZK) band += static_cast<float>(zk4[t]);
               if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
               s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
             }

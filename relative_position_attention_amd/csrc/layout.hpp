@@ -23,9 +23,13 @@
 //  * Key side: pitch = 1 (mod 8): for a key row j and four consecutive
 //    queries i1..i1+3 the entries Z^K[j, i-j+D] are four consecutive
 //    (ascending) elements, 4-aligned.
-//  * pad >= 4 and pitch >= pad + width + 4 leave margins of at least three
+//  * pad >= 8 and pitch >= pad + width + 4 leave margins of at least three
 //    elements on both sides of every row, so such a 4-run that holds at
 //    least one reachable entry never leaves its row.
+//  * The pads also make longer runs 16-byte aligned: on the query side the 64
+//    entries of one query row and one 64-key tile (j0 = 0 mod 64), on the key
+//    side the 128 entries of one key row and one 128-query block, start on an
+//    8-element boundary (the kernels stage them into LDS with 16-byte loads).
 #pragma once
 
 #include <cstdint>
@@ -93,10 +97,12 @@ RP_HD void key_group_window(int g, int N, int D, bool causal, int& slo, int& shi
 
 RP_HD int mod4(int x) { return ((x % 4) + 4) % 4; }
 
-// Column pads making the 4-runs aligned (see the header comment); base and
-// gG are multiples of 8.
-RP_HD int query_pad(int slo, int D) { return 4 + mod4(3 - D + slo); }
-RP_HD int key_pad(int slo, int D) { return 4 + mod4(slo - D); }
+RP_HD int mod8(int x) { return ((x % 8) + 8) % 8; }
+
+// Column pads making the 4-runs and the tile runs aligned (see the header
+// comment); base and gG are multiples of 8.
+RP_HD int query_pad(int slo, int D) { return 8 + mod8(7 - D + slo); }
+RP_HD int key_pad(int slo, int D) { return 8 + mod8(slo - D); }
 
 // Smallest pitch >= need with pitch = r (mod 8).
 RP_HD int pitch_mod8(int need, int r) { return need + ((r - need) % 8 + 8) % 8; }
