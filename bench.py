@@ -43,13 +43,42 @@ def credited_flops(spec):
     return fwd, 2.0 * fwd
 
 
-def attention_flops(spec):
-    """MFMA FLOPs of the forward attention kernel alone (QK^T and PV)."""
+def pair_flops(spec):
+    """2 d FLOPs per visible (query, key) pair: one N x N x d product."""
     B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
-    attn = 4.0 * B * H * N * N * d
+    f = 2.0 * B * H * N * N * d
     if spec["causal"]:
-        attn *= (N + 1) / (2.0 * N)
-    return attn
+        f *= (N + 1) / (2.0 * N)
+    return f
+
+
+KERNEL_SOURCE = {"attn_fwd": "fwd_fast.hip", "bwd_q": "bwd_q_fast.hip", "bwd_k": "bwd_k_fast.hip"}
+
+
+def measured_traffic(kernel, mech):
+    """HBM bytes per launch of `kernel` for mechanism `mech` from the committed
+    rocprofv3 counter summary (profiles/traffic_*.json), if that summary was
+    taken on the current kernel source (same SHA-256); else None."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "relative_position_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in [os.path.join(csrc, KERNEL_SOURCE[kernel])] + sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json"))):
+        with open(path) as fh:
+            rec = json.load(fh)
+        if rec.get("kernel") == f"{kernel} ({mech})" and rec.get("source_sha256") == digest:
+            return rec["hbm_bytes_per_launch"]
+    return None
+
+
+# Algorithmic MFMA work of each attention kernel, in N x N x d products:
+# forward QK^T, PV; query pass QK^T, dO V^T, dS K; key pass QK^T, dO V^T,
+# P^T dO, dS^T Q (the operand splits for peaked softmax are not counted).
+KERNEL_PRODUCTS = {"attn_fwd": 2, "bwd_q": 3, "bwd_k": 4}
 
 
 class MechRun:
@@ -75,7 +104,7 @@ class MechRun:
         self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
         self.grads = rpa.empty_grads(self.prob, dev)
         self.fwd_flops, self.bwd_flops = credited_flops(spec)
-        self.attn_flops = attention_flops(spec)
+        self.pair_flops = pair_flops(spec)
 
     def project(self, rpa):
         rpa.project(self.prob, self.t, z=self.z, ws=self.ws_f)
@@ -181,33 +210,49 @@ def main():
             r.backward(rpa)
     torch.cuda.synchronize()
 
-    marks = []
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    # per (step, mechanism): python-level marks around the projection, and
+    # the library's stage events around each kernel (relpos_set_stage_events)
+    marks = [[(ev_list_p, new_events(2), new_events(6)) for ev_list_p in
+              [new_events(2) for _ in runs]] for _ in range(args.steps)]
+    for row in marks:  # create every HIP event before the timed region
+        for pe, fe, be in row:
+            for e in pe + fe + be:
+                e.record(stream)
     torch.cuda.synchronize()
     t_start = ev()
-    for _ in range(args.steps):
-        row = []
-        for r in runs:
-            e0 = ev()
+    for step in range(args.steps):
+        for k, r in enumerate(runs):
+            pe, fe, be = marks[step][k]
+            pe[0].record(stream)
             r.project(rpa)
-            e1 = ev()
+            pe[1].record(stream)
+            rpa.set_stage_events(fe)
             r.attn(rpa)
-            e2 = ev()
+            rpa.set_stage_events(be)
             r.backward(rpa)
-            e3 = ev()
-            row.append((e0, e1, e2, e3))
-        marks.append(row)
+            rpa.set_stage_events([])
     t_end = ev()
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    def avg(fn):
+        return sum(fn(m) for m in marks) / args.steps
+
     per = {}
+    kernels = []  # (ms, mechanism, kernel)
     step_flops = 0.0
     for k, r in enumerate(runs):
-        proj = sum(m[k][0].elapsed_time(m[k][1]) for m in marks) / args.steps
-        attn = sum(m[k][1].elapsed_time(m[k][2]) for m in marks) / args.steps
-        bwd = sum(m[k][2].elapsed_time(m[k][3]) for m in marks) / args.steps
-        fwd = proj + attn
+        proj = avg(lambda m: m[k][0][0].elapsed_time(m[k][0][1]))
+        fwd = avg(lambda m: m[k][0][0].elapsed_time(m[k][1][1]))
+        attn = avg(lambda m: m[k][1][0].elapsed_time(m[k][1][1]))
+        bwd = avg(lambda m: m[k][2][0].elapsed_time(m[k][2][5]))
+        kq = avg(lambda m: m[k][2][1].elapsed_time(m[k][2][2]))
+        kk = avg(lambda m: m[k][2][3].elapsed_time(m[k][2][4]))
+        kernels += [(attn, r, "attn_fwd"), (kq, r, "bwd_q"), (kk, r, "bwd_k")]
         step_flops += r.fwd_flops + r.bwd_flops
         d = {
             "shape": {x: r.spec[x] for x in ("B", "H", "N", "causal")},
@@ -217,22 +262,32 @@ def main():
             "bwd_tflops": round(r.bwd_flops / bwd / 1e9, 2),
             "fwd_pct_peak": round(100 * r.fwd_flops / fwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
             "bwd_pct_peak": round(100 * r.bwd_flops / bwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
-            "attn_kernel_tflops": round(r.attn_flops / attn / 1e9, 2),
+            "kernel_ms": {"attn_fwd": round(attn, 4), "bwd_q": round(kq, 4),
+                          "bwd_k": round(kk, 4)},
+            "kernel_mfma_tflops": {
+                name: round(KERNEL_PRODUCTS[name] * r.pair_flops / ms / 1e9, 2)
+                for name, ms in (("attn_fwd", attn), ("bwd_q", kq), ("bwd_k", kk))},
         }
         if r.name in mem:
             d["fwd_peak_mib"] = round(mem[r.name][0], 1)
             d["bwd_peak_mib"] = round(mem[r.name][1], 1)
         per[r.name] = d
 
-    # Dominant single-launch kernel timed live: the forward attention kernel
-    # (relpos_attn_fwd with retained projections is exactly one launch).
-    dom = max(runs, key=lambda r: per[r.name]["attn_kernel_ms"])
-    dom_ms = per[dom.name]["attn_kernel_ms"]
-    achieved = dom.attn_flops / dom_ms / 1e9
-    roofline = {"bound": "mfma", "kernel": f"attn_fwd_kernel ({dom.name})",
+    # Dominant kernel: the single attention kernel (forward, query pass or key
+    # pass) with the longest average launch, timed live with the library's
+    # stage events on the launch stream; its algorithmic MFMA FLOPs per launch
+    # over that duration.
+    dom_ms, dom, dom_kernel = max(kernels, key=lambda x: x[0])
+    achieved = KERNEL_PRODUCTS[dom_kernel] * dom.pair_flops / dom_ms / 1e9
+    roofline = {"bound": "mfma", "kernel": f"{dom_kernel} ({dom.name})",
+                "avg_launch_ms": round(dom_ms, 4),
+                "flops_per_launch": KERNEL_PRODUCTS[dom_kernel] * dom.pair_flops,
                 "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom_kernel, dom.name)}
+    if roofline["traffic"] is not None:
+        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, copy-calibrated)"
+        roofline["traffic_tb_per_s"] = round(roofline["traffic"] / dom_ms / 1e9, 3)
 
     value = step_flops / ms_per_step / 1e9
     out = {

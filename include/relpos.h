@@ -206,6 +206,20 @@ int relpos_attn_bwd(const relpos_desc *desc, const relpos_shape *shape,
                     const void *o, const float *lse, const void *dout,
                     relpos_grads *grads, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * relpos_set_stage_events -- instrumentation, host only (not a step of the
+ * method).  Registers up to 8 hipEvent_t handles, passed as void*, for the
+ * calling thread; the entry points called afterwards on this thread record
+ * them on their stream: relpos_attn_fwd records [0] before and [1] after its
+ * attention kernel; relpos_attn_bwd records [0] before preprocessing, [1]
+ * after it, [2] after the query-parallel pass, [3] before the key-parallel
+ * pass, [4] after it and [5] at its end.  Handles beyond `count` are not
+ * recorded; count = 0 clears the registration.  The events stay owned by the
+ * caller and must outlive the calls that record them.
+ * Errors: INVALID_ARG (count outside [0, 8], or events NULL with count > 0).
+ */
+int relpos_set_stage_events(void *const *events, int32_t count);
+
 /* Static description of a return code. */
 const char *relpos_strerror(int code);
 

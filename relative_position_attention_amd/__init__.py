@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     attn_fwd,
     attn_bwd,
     empty_grads,
+    set_stage_events,
     strerror,
     EXPORTED_SYMBOLS,
 )

@@ -9,6 +9,7 @@ LIB_NAME = "librelpos.so"
 EXPORTED_SYMBOLS = (
     "relpos_plan_sizes", "relpos_plan_rows", "relpos_project", "relpos_attn_fwd",
     "relpos_attn_bwd", "relpos_strerror", "relpos_last_error", "relpos_abi_version",
+    "relpos_set_stage_events",
 )
 
 ABI_VERSION = 2
@@ -100,6 +101,7 @@ def library():
         lib.relpos_last_error.restype = ctypes.c_char_p
         lib.relpos_last_error.argtypes = []
         lib.relpos_abi_version.restype = ctypes.c_int
+        lib.relpos_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
         if lib.relpos_abi_version() != ABI_VERSION:
             raise RuntimeError("librelpos.so ABI version mismatch")
         _LIB = lib
@@ -310,3 +312,17 @@ def attn_bwd(problem, t, o, lse, dout, z=None, grads=None, ws=None):
                                      _ptr(dout), ctypes.byref(gr), _ptr(ws), ws.numel(),
                                      _stream()), "relpos_attn_bwd")
     return grads
+
+
+def set_stage_events(events):
+    """Register torch.cuda.Event objects (up to 8) that the following entry
+    points on this thread record around their kernels (instrumentation; see
+    relpos_set_stage_events in include/relpos.h).  [] clears."""
+    import torch
+    handles = []
+    for ev in events:
+        if ev.cuda_event == 0:  # torch creates the HIP event on first record
+            ev.record(torch.cuda.current_stream())
+        handles.append(ev.cuda_event)
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    _check(library().relpos_set_stage_events(arr, len(handles)), "relpos_set_stage_events")

@@ -19,6 +19,28 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Stage events (instrumentation): hipEvent_t handles the entry points record
+// on their stream around their kernels, for timing single kernels.
+constexpr int kMaxStageEvents = 8;
+thread_local void* g_stage_events[kMaxStageEvents] = {};
+thread_local int g_stage_event_count = 0;
+
+int mark(int k, hipStream_t s) {
+  if (k < g_stage_event_count && g_stage_events[k] != nullptr) {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(g_stage_events[k]), s);
+    if (e != hipSuccess) {
+      g_last_error = std::string("hipEventRecord: ") + hipGetErrorString(e);
+      return RELPOS_E_HIP;
+    }
+  }
+  return RELPOS_OK;
+}
+#define RP_MARK(k)                                      \
+  do {                                                  \
+    int rc_ = mark((k), s);                             \
+    if (rc_ != RELPOS_OK) return rc_;                   \
+  } while (0)
+
 // Host plans are cached per thread, keyed by the descriptor's contents (the
 // explicit map rows included) and the shape: building one evaluates the map
 // over every offset, far more host time than enqueuing the kernels.
@@ -384,10 +406,12 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   a.o = o;
   a.lse = lse;
   const int ff = base_flags(p) | (p.split ? F_SPLIT : 0);
+  RP_MARK(0);
   if (p.dtype == RELPOS_DTYPE_F32)
     RP_HIP(launch_attn_fwd(0, ff, a, p.B, s));
   else
     RP_HIP(launch_attn_fwd_bf16(ff, a, p.B, s));
+  RP_MARK(1);
   return RELPOS_OK;
 }
 
@@ -435,7 +459,9 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int64_t rows = static_cast<int64_t>(p.BH) * p.N;
 
   // Preprocessing: D = rowdot(dO, O)
+  RP_MARK(0);
   RP_HIP(launch_rowdot(dt, p.out_dtype == RELPOS_DTYPE_F32, o, dout, dvec, rows, s));
+  RP_MARK(1);
 
   AttnArgs a = attn_args(p, in, z, ws);
   a.dout = dout;
@@ -458,6 +484,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     RP_HIP(launch_attn_bwd_q(dt, qflags, a, p.B, s));
   else
     RP_HIP(launch_bwd_q_bf16(qflags, a, p.B, s));
+  RP_MARK(2);
   {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
@@ -549,10 +576,12 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
 
   // Key-parallel pass, then the key reduction
   const int kflags = bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0);
+  RP_MARK(3);
   if (dt == 0)
     RP_HIP(launch_attn_bwd_k(dt, kflags, a, p.B, s));
   else
     RP_HIP(launch_bwd_k_bf16(kflags, a, p.B, s));
+  RP_MARK(4);
   {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
@@ -627,6 +656,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     du.N = p.N;
     RP_HIP(launch_du(dt, du, s));
   }
+  RP_MARK(5);
   return RELPOS_OK;
 }
 
@@ -735,6 +765,16 @@ const char* relpos_strerror(int code) {
 }
 
 const char* relpos_last_error(void) { return g_last_error.c_str(); }
+
+int relpos_set_stage_events(void* const* events, int32_t count) {
+  if (count < 0 || count > kMaxStageEvents || (count > 0 && events == nullptr)) {
+    g_last_error = "stage event count must be in [0, 8]";
+    return RELPOS_E_INVALID_ARG;
+  }
+  for (int k = 0; k < kMaxStageEvents; ++k) g_stage_events[k] = k < count ? events[k] : nullptr;
+  g_stage_event_count = count;
+  return RELPOS_OK;
+}
 
 int relpos_abi_version(void) { return RELPOS_ABI_VERSION; }
 

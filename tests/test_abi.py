@@ -157,3 +157,15 @@ def test_explicit_contiguous_map_accepted():
 def test_strerror():
     assert rpa.strerror(0) == "success"
     assert rpa.strerror(-5) == "buffer too small"
+
+
+@needs_lib
+def test_stage_events_validation():
+    # instrumentation hook: host-only validation, no GPU call
+    import ctypes
+    lib = rpa.library()
+    assert lib.relpos_set_stage_events(None, 0) == 0
+    arr = (ctypes.c_void_p * 9)()
+    assert lib.relpos_set_stage_events(arr, 9) == -1
+    assert lib.relpos_set_stage_events(None, 2) == -1
+    assert lib.relpos_set_stage_events(arr, 0) == 0
