@@ -281,7 +281,10 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.D = p.delta;
     pa.S = p.S;
     pa.NG = p.NG;
-    RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zq), s));
+    if (dt == 0)
+      RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zq), s));
+    else
+      RP_HIP(launch_project_bf16(pa, p.BH, s));
   }
   if (p.ak) {
     ProjectArgs pa;
@@ -297,7 +300,10 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.D = p.delta;
     pa.S = p.S;
     pa.NG = p.NG;
-    RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zk), s));
+    if (dt == 0)
+      RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zk), s));
+    else
+      RP_HIP(launch_project_bf16(pa, p.BH, s));
   }
   RowKeyArgs rk;
   rk.q = in->q;

@@ -42,7 +42,7 @@ constexpr int kKP = 72;            // K and V tile pitch (bf16): 144-byte rows
 constexpr float kLazy = 8.f;       // rescale threshold, log2 units
 
 template <int F>
-__global__ __launch_bounds__(256, 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
+__global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
                                                           int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
