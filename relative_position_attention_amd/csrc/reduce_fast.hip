@@ -27,46 +27,68 @@ namespace {
 constexpr int kRP = 72;   // LDS pitch of bf16 tiles (144-byte rows)
 constexpr int kFP = 68;   // LDS pitch of fp32 tiles
 
-// Stage dZ~ for tokens r0 .. r0+63 (one group) and expanded rows s0 .. s0+63
-// into zt (bf16, [token][s]) and optionally zf (fp32).  Entries outside the
-// token's reachable band rows [max(smin, 1), min(smax, 2D-1)] are zero.
-template <typename GT, bool F32COPY>
-__device__ __forceinline__ void stage_dz(const Rsrc& rz, const GroupInfo& gi, int g0, int r0,
-                                         int s0, int N, int D, bool key_side, bool causal,
-                                         bf16* zt, float* zf) {
-  constexpr int VEC = 16 / sizeof(GT);
-  constexpr int NCH = 64 / VEC + 1;  // aligned chunks covering 64 entries
-  const int tid = threadIdx.x;
-  const int r = tid >> 2, tq = tid & 3;
-  const int i = r0 + r;
-  int smin = 1, smax = 0;
-  if (i < N) {
-    if (key_side)
-      key_s_range(i, N, D, causal, smin, smax);
-    else
-      query_s_range(i, N, D, causal, smin, smax);
-  }
-  smin = imax(smin, 1);
-  smax = imin(smax, 2 * D - 1);
-  const int rowbase = gi.base + (i - g0) * gi.pitch;          // element offset of column 0
-  const int e0 = rowbase + (s0 - gi.slo + gi.pad);            // element of s0
-  const int c_first = e0 & ~(VEC - 1);
-  for (int ch = tq; ch < NCH; ch += 4) {
-    const int ce = c_first + ch * VEC;
-    if (ce > e0 + 63) break;
-    const uint4 w = bload16(rz, ce >= 0 ? static_cast<uint32_t>(ce) * sizeof(GT) : kOob);
-    GT vals[VEC];
-    __builtin_memcpy(vals, &w, 16);
+// One (64 tokens x 64 expanded rows s0 .. s0+63) tile of dZ~, moved in two
+// phases so the next tile's loads overlap the current tile's products: load()
+// issues the aligned 16-byte chunk loads of this thread's token row into
+// registers, store() writes them to LDS as zt (bf16, [token][s]) and
+// optionally zf (fp32).  Entries outside the token's reachable band rows
+// [max(smin, 1), min(smax, 2D-1)] are written as zero.  Thread t moves token
+// row t / 4, chunks t % 4, t % 4 + 4, ...
+template <typename GT>
+struct DzTile {
+  static constexpr int VEC = 16 / sizeof(GT);
+  static constexpr int NCH = 64 / VEC + 1;  // aligned chunks covering 64 entries
+  static constexpr int PER = (NCH + 3) / 4;
+  uint4 w[PER];
+  int e0;      // element index of s0 in the token's row
+  int lo, hi;  // reachable positions s - s0 of the token (empty past N)
+
+  __device__ __forceinline__ void load(const Rsrc& rz, const GroupInfo& gi, int g0, int r0, int s0,
+                                       int N, int D, bool key_side, bool causal) {
+    const int tid = threadIdx.x, r = tid >> 2, tq = tid & 3;
+    const int i = r0 + r;
+    int smin = 1, smax = 0;
+    if (i < N) {
+      if (key_side)
+        key_s_range(i, N, D, causal, smin, smax);
+      else
+        query_s_range(i, N, D, causal, smin, smax);
+    }
+    lo = imax(smin, 1) - s0;
+    hi = imin(smax, 2 * D - 1) - s0;
+    e0 = gi.base + (i - g0) * gi.pitch + (s0 - gi.slo + gi.pad);
+    const int cf = e0 & ~(VEC - 1);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int s = s0 + (ce + e - e0);
-      if (s < s0 || s > s0 + 63) continue;
-      const float v = (i < N && s >= smin && s <= smax) ? to_f(vals[e]) : 0.f;
-      zt[r * kRP + (s - s0)] = static_cast<bf16>(v);
-      if (F32COPY) zf[r * kFP + (s - s0)] = v;
+    for (int u = 0; u < PER; ++u) {
+      const int ch = tq + 4 * u;
+      const int ce = cf + ch * VEC;
+      const bool ok = ch < NCH && ce >= 0 && ce <= e0 + 63 && hi >= 0 && lo <= 63 && lo <= hi;
+      w[u] = bload16(rz, ok ? static_cast<uint32_t>(ce) * sizeof(GT) : kOob);
     }
   }
-}
+
+  template <bool F32COPY>
+  __device__ __forceinline__ void store(bf16* zt, int zpitch, float* zf, int fpitch) const {
+    const int tid = threadIdx.x, r = tid >> 2, tq = tid & 3;
+    const int cf = e0 & ~(VEC - 1);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int ch = tq + 4 * u;
+      if (ch >= NCH) continue;
+      const int p0 = cf + ch * VEC - e0;
+      GT vals[VEC];
+      __builtin_memcpy(vals, &w[u], 16);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int p = p0 + e;
+        if (p < 0 || p > 63) continue;
+        const float v = (p >= lo && p <= hi) ? to_f(vals[e]) : 0.f;
+        zt[r * zpitch + p] = static_cast<bf16>(v);
+        if (F32COPY) zf[r * fpitch + p] = v;
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------- finalize
 
@@ -77,7 +99,10 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
   const int h = bh % f.H;
-  const int r0 = blockIdx.x * 64;
+  // widest windows first: under a causal map the last query blocks and the
+  // first key blocks reach the most rows
+  const int rbk = static_cast<int>(blockIdx.x);
+  const int r0 = (f.key_side ? rbk : static_cast<int>(gridDim.x) - 1 - rbk) * 64;
   const int64_t tok = static_cast<int64_t>(bh) * f.N;
   const int D = f.D;
   floatx4 acc[4];
@@ -99,19 +124,23 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
     const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(f.dz) + static_cast<int64_t>(bh) * f.dz_bh,
                               static_cast<uint64_t>(f.dz_bh) * sizeof(GT));
     const Rsrc ra = make_rsrc(atab, static_cast<uint64_t>(f.S) * 128);
-    for (int s0 = sa; s0 <= sb; s0 += 64) {
-      stage_dz<GT, false>(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0, zt,
-                          nullptr);
-      {
-        // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
-        const int ar = tid >> 2, ac = (tid & 3) * 16;
+    // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
+    const int ar = tid >> 2, ac = (tid & 3) * 16;
+    DzTile<GT> dt;
+    uint4 ta[2];
+    auto load_stage = [&](int s0) {
+      dt.load(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint4 w = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
-          *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = w;
-        }
-      }
+      for (int u = 0; u < 2; ++u)
+        ta[u] = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
+    };
+    if (sa <= sb) load_stage(sa);
+    for (int s0 = sa; s0 <= sb; s0 += 64) {
+      dt.template store<false>(zt, kRP, nullptr, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = ta[u];
       __syncthreads();
+      if (s0 + 64 <= sb) load_stage(s0 + 64);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
@@ -178,10 +207,24 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   __shared__ float bsh[2][64];
   __shared__ float p2red[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int s0 = blockIdx.x * 64;
+  const int D = p.D;
+  // s tiles from the one holding offset 0 (s = D) outwards: those reach the
+  // most tokens, so the longest blocks start first
+  int tile;
+  {
+    const int T = static_cast<int>(gridDim.x), c = imin(D / 64, T - 1);
+    const int below = c, above = T - 1 - c, mm = imin(below, above);
+    const int k = static_cast<int>(blockIdx.x) - 1;
+    if (k < 0)
+      tile = c;
+    else if (k < 2 * mm)
+      tile = (k & 1) ? c - (k / 2 + 1) : c + (k / 2 + 1);
+    else
+      tile = above > below ? c + mm + 1 + (k - 2 * mm) : c - mm - 1 - (k - 2 * mm);
+  }
+  const int s0 = tile * 64;
   const int h = blockIdx.y;
   const int chunk = blockIdx.z;
-  const int D = p.D;
   const int nrb = (p.N + 63) / 64;
   const int total = p.B * nrb;
   const int per = (total + p.nchunk - 1) / p.nchunk;
@@ -198,45 +241,69 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   float bx0 = 0.f, bx1 = 0.f;  // boundary P1 (threads < 64: d = tid)
   float bs0 = 0.f, bs1 = 0.f;  // boundary P2 (every thread < 64, same order)
 
-  for (int sb = sb0; sb < sb1; ++sb) {
-    const int b = sb / nrb, rb = sb % nrb;
-    const int r0 = rb * 64;
-    const int grp = r0 / kGroup;
+  // does row block sb reach this block's band rows (uniform)
+  auto band_hit = [&](int sb) {
+    const int grp = ((sb % nrb) * 64) / kGroup;
     int slo, shi;
     if (p.key_side)
       key_group_window(grp, p.N, D, p.causal != 0, slo, shi);
     else
       query_group_window(grp, p.N, D, p.causal != 0, slo, shi);
     const int sa = imax(1, slo), se = imin(2 * D - 1, shi);
-    const bool band_hit = D >= 1 && sa <= se && s0 <= se && s0 + 63 >= sa;
-    if (!band_hit && !has0 && !has2) continue;  // uniform
+    return D >= 1 && sa <= se && s0 <= se && s0 + 63 >= sa;
+  };
+  auto next_stage = [&](int sb) {
+    while (sb < sb1 && !(has0 || has2 || band_hit(sb))) ++sb;
+    return sb;
+  };
+
+  DzTile<GT> dt;
+  uint4 tx[2];
+  float tb[2] = {0.f, 0.f};
+  bool hit_next = false;
+  const int xr = tid >> 2, xc = (tid & 3) * 16;
+  auto load_stage = [&](int sb) {
+    const int b = sb / nrb, r0 = (sb % nrb) * 64;
+    const int grp = r0 / kGroup;
     const int64_t bhs = static_cast<int64_t>(b) * p.H + h;
     const int64_t tok = bhs * p.N;
     if (want_p1) {
       const Rsrc rx = make_rsrc(reinterpret_cast<const bf16*>(p.x) + tok * 64,
                                 static_cast<uint64_t>(p.N) * 128);
-      const int xr = tid >> 2, xc = (tid & 3) * 16;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint4 w = bload16(rx, static_cast<uint32_t>((r0 + xr) * 128 + (xc + 8 * u) * 2));
-        *reinterpret_cast<uint4*>(&xt[xr * kRP + xc + 8 * u]) = w;
-      }
+      for (int u = 0; u < 2; ++u)
+        tx[u] = bload16(rx, static_cast<uint32_t>((r0 + xr) * 128 + (xc + 8 * u) * 2));
     }
-    if (band_hit) {
+    hit_next = band_hit(sb);
+    if (hit_next) {
       const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(p.dz) + bhs * p.dz_bh,
                                 static_cast<uint64_t>(p.dz_bh) * sizeof(GT));
-      stage_dz<GT, true>(rz, p.gi[grp], grp * kGroup, r0, s0, p.N, D, p.key_side != 0,
-                         p.causal != 0, zt, zf);
+      dt.load(rz, p.gi[grp], grp * kGroup, r0, s0, p.N, D, p.key_side != 0, p.causal != 0);
     }
-    if (has0 || has2) {
-      if (tid < 64) {
-        const int i = r0 + tid;
-        bsh[0][tid] = i < p.N ? p.bnd[(tok + i) * 2 + 0] : 0.f;
-        bsh[1][tid] = i < p.N ? p.bnd[(tok + i) * 2 + 1] : 0.f;
-      }
+    if ((has0 || has2) && tid < 64) {
+      const int i = r0 + tid;
+      tb[0] = i < p.N ? p.bnd[(tok + i) * 2 + 0] : 0.f;
+      tb[1] = i < p.N ? p.bnd[(tok + i) * 2 + 1] : 0.f;
+    }
+  };
+
+  int sb = next_stage(sb0);
+  if (sb < sb1) load_stage(sb);
+  while (sb < sb1) {
+    const bool hit = hit_next;
+    if (want_p1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&xt[xr * kRP + xc + 8 * u]) = tx[u];
+    }
+    if (hit) dt.template store<true>(zt, kRP, zf, kFP);
+    if ((has0 || has2) && tid < 64) {
+      bsh[0][tid] = tb[0];
+      bsh[1][tid] = tb[1];
     }
     __syncthreads();
-    if (band_hit) {
+    const int nsb = next_stage(sb + 1);
+    if (nsb < sb1) load_stage(nsb);
+    if (hit) {
       if (want_p1) {
         // P1 (s x d) += Z^T (s x tokens) X (tokens x d); K axis (tokens) in
         // the order 32c + 4g + e, 32c + 16 + 4g + e
@@ -291,6 +358,7 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
       }
     }
     __syncthreads();
+    sb = nsb;
   }
 
   // write the chunk's partials
