@@ -11,9 +11,10 @@
 //   wave's keys in registers), each lane owning one key column and four
 //   consecutive queries per 16-query block;
 //   relation terms exactly as the forward (same boundary-entry rule);
-//   P = exp2(S tau log2 e - L log2 e), G = tau P (dP - D);
-//   dV^T += dO^T P and dK^T += Q^T G on MFMA (dO^T and Q^T read with the
-//   transposing LDS read; P and G as bf16, or bf16 hi + lo under F_SPLIT).
+//   P = exp2(S tau log2 e - L log2 e), G' = P (dP - D) (G = tau G'; tau
+//   multiplies the finished sums instead);
+//   dV^T += dO^T P and dK^T += Q^T G' on MFMA (dO^T and Q^T read with the
+//   transposing LDS read; P and G' as bf16, or bf16 hi + lo under F_SPLIT).
 // Key offset gradients ([RPA] §4.2): a band pair writes G to
 // dZ~^K[j, delta + D] (single writer, aligned 4-entry runs); pairs with
 // |delta| >= D add into two fp32 per-key boundary sums; with the
@@ -191,14 +192,19 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     if (it >= itw) {
       const bf16* Qs = sq[buf];
       const bf16* Ds = sd[buf];
+      // region of the tile for this wave (uniform); on saturated tiles the
+      // key's boundary entry is the initial value of the S accumulator
+      const bool sat_lo = it < n_lo, sat_hi = it >= t_hi;
       floatx4 s[2][2], dp[2][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const float k0 = (KC && (sat_lo || sat_hi)) ? (sat_hi ? khi[kb] : klo[kb]) : 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb][kb] = floatx4{k0, k0, k0, k0};
           dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -213,24 +219,31 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         }
       }
 
-      const bool sat_lo = it < n_lo, sat_hi = it >= t_hi;
       const bool need_mask = (i0 + kT > N) || (jw + 32 > N) || (CAUSAL && i0 < jw + 31);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int i1 = i0 + 16 * qb + 4 * g;
         const int qo = 16 * qb + 4 * g;
         const floatx4 ql2 = *reinterpret_cast<const floatx4*>(&sqs[buf][0][qo]);
-        const floatx4 qdd = *reinterpret_cast<const floatx4*>(&sqs[buf][1][qo]);
         const floatx4 qrl = *reinterpret_cast<const floatx4*>(&sqs[buf][2][qo]);
         const floatx4 qrh = *reinterpret_cast<const floatx4*>(&sqs[buf][3][qo]);
+        if (sat_lo || sat_hi) {
+          // saturated tile: the query's entry and L fold into one offset per
+          // query (the key's entry is already in the accumulator)
+          float cq[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) cq[t] = fmaf(sat_hi ? qrh[t] : qrl[t], sl2, -ql2[t]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t], sl2, cq[t]));
+          continue;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int j = jw + 16 * kb + c16;
           float rel[4];
-          if (sat_lo || sat_hi) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) rel[t] = sat_hi ? (qrh[t] + khi[kb]) : (qrl[t] + klo[kb]);
-          } else {
+          {
             float zk[4] = {0.f, 0.f, 0.f, 0.f};
             if (F & F_ZK) {
               const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
@@ -255,16 +268,33 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
             }
           }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float p = fast_exp2(fmaf(s[qb][kb][t] + rel[t], sl2, -ql2[t]));
-            if (need_mask) {
-              const int i = i1 + t;
-              if (j >= N || (CAUSAL && j > i)) p = 0.f;
-            }
-            s[qb][kb][t] = p;
-            dp[qb][kb][t] = tau * p * (dp[qb][kb][t] - qdd[t]);
-          }
+          for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t] + rel[t], sl2, -ql2[t]));
         }
+      }
+      if (need_mask) {
+        // (the empty asm keeps this a branch: without it the compiler turns
+        // the rare masked pass into selects on every tile)
+        asm volatile("");
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const int j = jw + 16 * kb + c16;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int i = i0 + 16 * qb + 4 * g + t;
+              if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = 0.f;
+            }
+          }
+      }
+      // G' = P (dP - D)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const floatx4 qdd = *reinterpret_cast<const floatx4*>(&sqs[buf][1][16 * qb + 4 * g]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) dp[qb][kb][t] = s[qb][kb][t] * (dp[qb][kb][t] - qdd[t]);
       }
 
       // key offset gradients and column sums
@@ -296,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
                   else if (dl <= -D)
                     blo[kb] += gg;
                   else {
-                    bandv = gg;
+                    bandv = tau * gg;
                     any = any || (i < N && j < N && (!CAUSAL || j <= i));
                   }
                   run[t] = bandv;  // ascending columns
@@ -363,15 +393,16 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int j = jw + 16 * kb + c16;
-    const float lo = wave_sum_g(blo[kb]);
-    const float hi = wave_sum_g(bhi[kb]);
-    const float cs = wave_sum_g(csum[kb]);
+    const float lo = tau * wave_sum_g(blo[kb]);
+    const float hi = tau * wave_sum_g(bhi[kb]);
+    const float cs = tau * wave_sum_g(csum[kb]);
     if (j >= N) continue;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       float dvv[4] = {dv[kb][db][0], dv[kb][db][1], dv[kb][db][2], dv[kb][db][3]};
       store_out4(a.dv, (tok + j) * 64 + 16 * db + 4 * g, a.out_f32 != 0, dvv);
-      float dkv[4] = {dk[kb][db][0], dk[kb][db][1], dk[kb][db][2], dk[kb][db][3]};
+      float dkv[4] = {tau * dk[kb][db][0], tau * dk[kb][db][1], tau * dk[kb][db][2],
+                      tau * dk[kb][db][3]};
       store4(a.dkacc + (tok + j) * 64 + 16 * db + 4 * g, dkv);
     }
     if (g == 0) {

@@ -9,8 +9,9 @@
 // boundary-entry rule) and, from the saved logsumexp L and D = rowdot(dO, O)
 // ([RPA] §3.1 Eq. (3), App. B tile-locality lemma):
 //   S^T = K Q^T and dP^T = V dO^T on MFMA (A from LDS rows, B in registers),
-//   P = exp2(S tau log2 e - L log2 e), G = tau P (dP - D),
-//   dQ^T += K^T G^T on MFMA (K^T read with the transposing LDS read; G as
+//   P = exp2(S tau log2 e - L log2 e), G' = P (dP - D) (the gradient of the
+//   scores is G = tau G'; tau multiplies the finished sums instead),
+//   dQ^T += K^T G'^T on MFMA (K^T read with the transposing LDS read; G' as
 //   bf16, or bf16 hi + lo under F_SPLIT).
 // Offset gradients ([RPA] §4.2): a band pair (|delta| < D) writes its G to
 // dZ~^Q[i, delta + D] -- one entry per (query, offset), a single writer,
@@ -172,14 +173,22 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
       const bf16* Vs = sv[buf];
+      // region of the tile for this wave (uniform): saturated tiles take one
+      // entry per query (off) and one per key, the latter as the initial
+      // value of the S accumulator
+      const bool sat = kt < n_hi || kt >= t_lo;
+      const int side = kt < n_hi ? 1 : 0;
       floatx4 s[2][4], dp[2][4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int kb = 0; kb < 4; ++kb) {
+        floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (KC && sat) kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb][kb] = kx;
           dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -196,21 +205,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 
       // relation terms (same values as the forward); off = the row's
       // constant on saturated tiles
-      const bool sat = kt < n_hi || kt >= t_lo;
-      const int side = kt < n_hi ? 1 : 0;
       float off[2];
       if (sat) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) off[qb] = side ? rhi[qb] : rlo[qb];
-        if (KC) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const floatx4 kx =
-                *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) s[qb][kb] += kx;
-          }
-        }
       } else {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -256,23 +254,38 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       }
       const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw);
 
-      // P and G = tau P (dP - D), in place of s
+      // P, then G' = P (dP - D) in place of s; tau is applied to the sums
+      // of G' (dQ, the boundary sums) and to the band entries as written
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int i = iw + 16 * qb + c16;
         const float bias = off[qb] * sl2 - l2[qb];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float p = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
-            if (need_mask) {
-              const int j = j0 + 16 * kb + 4 * g + t;
-              if (j >= N || (CAUSAL && j > i)) p = 0.f;
-            }
-            s[qb][kb][t] = tau * p * (dp[qb][kb][t] - dd[qb]);
-          }
+          for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
       }
+      if (need_mask) {
+        // (the empty asm keeps this a branch: without it the compiler turns
+        // the rare masked pass into selects on every tile)
+        asm volatile("");
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int i = iw + 16 * qb + c16;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int j = j0 + 16 * kb + 4 * g + t;
+              if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = 0.f;
+            }
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s[qb][kb][t] *= dp[qb][kb][t] - dd[qb];
 
       // offset gradients of the queries
       if (DZ) {
@@ -302,13 +315,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
                 const int j = j1 + t;
                 const int dl = i - j;
                 const float gg = s[qb][kb][t];
-                float bandv = 0.f;
+                float bandv = 0.f;  // tau G' for the band entry
                 if (dl >= D)
                   bhi[qb] += gg;
                 else if (dl <= -D)
                   blo[qb] += gg;
                 else {
-                  bandv = gg;
+                  bandv = tau * gg;
                   any = any || (i < N && j < N && (!CAUSAL || j <= i));
                 }
                 run[3 - t] = bandv;  // descending columns
@@ -361,12 +374,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int i = iw + 16 * qb + c16;
-    const float lo = wave_sum_g(blo[qb]);
-    const float hi = wave_sum_g(bhi[qb]);
+    const float lo = tau * wave_sum_g(blo[qb]);
+    const float hi = tau * wave_sum_g(bhi[qb]);
     if (i >= N) continue;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      float vals[4] = {dq[qb][db][0], dq[qb][db][1], dq[qb][db][2], dq[qb][db][3]};
+      float vals[4] = {tau * dq[qb][db][0], tau * dq[qb][db][1], tau * dq[qb][db][2],
+                       tau * dq[qb][db][3]};
       store4(a.dqacc + (tok + i) * 64 + 16 * db + 4 * g, vals);
     }
     if (DZ && g == 0) {

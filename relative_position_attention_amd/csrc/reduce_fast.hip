@@ -8,7 +8,10 @@
 // at column s - slo_g + pad_g.  Both kernels stage (64 tokens x 64 rows s)
 // tiles of it into LDS with aligned 16-byte loads (each token row's segment
 // is contiguous; entries a token cannot reach, and the two boundary rows, are
-// written as zero) and run the products on MFMA:
+// written as zero).  The tile is kept in fp32 with each token row shifted by
+// its own misalignment (e0 mod the chunk width), so the LDS writes stay whole
+// 16-byte chunks; the readers add the row's shift, kept beside the tile, and
+// round to bf16 when they build the MFMA operands:
 //   finalize_fast:  out = acc + dZ~ A~ (band rows) + the two boundary sums
 //                   times A~[0], A~[2D] in fp32 (+ column sums times u);
 //                   dQ = tau dS K + dZ^Q A^Q of the table-gradient lemma, the
@@ -25,13 +28,14 @@ namespace relpos {
 namespace {
 
 constexpr int kRP = 72;   // LDS pitch of bf16 tiles (144-byte rows)
-constexpr int kFP = 68;   // LDS pitch of fp32 tiles
+constexpr int kSP = 76;   // LDS pitch of the row-shifted fp32 dZ~ tiles
 
 // One (64 tokens x 64 expanded rows s0 .. s0+63) tile of dZ~, moved in two
 // phases so the next tile's loads overlap the current tile's products: load()
 // issues the aligned 16-byte chunk loads of this thread's token row into
-// registers, store() writes them to LDS as zt (bf16, [token][s]) and
-// optionally zf (fp32).  Entries outside the token's reachable band rows
+// registers, store() writes them to LDS as fp32 chunks at their memory
+// alignment: entry s0 + p of token row r sits at zf[r][p + so[r]], so[r] =
+// e0 mod VEC.  Entries outside the token's reachable band rows
 // [max(smin, 1), min(smax, 2D-1)] are written as zero.  Thread t moves token
 // row t / 4, chunks t % 4, t % 4 + 4, ...
 template <typename GT>
@@ -67,34 +71,52 @@ struct DzTile {
     }
   }
 
-  template <bool F32COPY>
-  __device__ __forceinline__ void store(bf16* zt, int zpitch, float* zf, int fpitch) const {
+  __device__ __forceinline__ void store(float* zf, int* so) const {
     const int tid = threadIdx.x, r = tid >> 2, tq = tid & 3;
-    const int cf = e0 & ~(VEC - 1);
+    const int o = e0 & (VEC - 1);
+    if (tq == 0) so[r] = o;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int ch = tq + 4 * u;
       if (ch >= NCH) continue;
-      const int p0 = cf + ch * VEC - e0;
-      GT vals[VEC];
-      __builtin_memcpy(vals, &w[u], 16);
+      const int p0 = VEC * ch - o;  // position s - s0 of the chunk's first entry
+      float f[VEC];
+      if constexpr (sizeof(GT) == 4) {
+        __builtin_memcpy(f, &w[u], 16);
+      } else {
+        const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const int p = p0 + e;
-        if (p < 0 || p > 63) continue;
-        const float v = (p >= lo && p <= hi) ? to_f(vals[e]) : 0.f;
-        zt[r * zpitch + p] = static_cast<bf16>(v);
-        if (F32COPY) zf[r * fpitch + p] = v;
+        for (int k = 0; k < 4; ++k) {
+          f[2 * k] = __uint_as_float(wd[k] << 16);
+          f[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+        }
       }
+      if (!(p0 >= lo && p0 + VEC - 1 <= hi)) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (p0 + e < lo || p0 + e > hi) f[e] = 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < VEC / 4; ++k)
+        *reinterpret_cast<floatx4*>(&zf[r * kSP + VEC * ch + 4 * k]) =
+            floatx4{f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]};
     }
   }
 };
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<bf16>(v[e]);
+  return r;
+}
 
 // ---------------------------------------------------------------- finalize
 
 template <typename GT>
 __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
-  __shared__ __attribute__((aligned(16))) bf16 zt[64 * kRP];
+  __shared__ __attribute__((aligned(16))) float zf[64 * kSP];
+  __shared__ int so[64];
   __shared__ __attribute__((aligned(16))) bf16 at[64 * kRP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
@@ -136,7 +158,7 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
     };
     if (sa <= sb) load_stage(sa);
     for (int s0 = sa; s0 <= sb; s0 += 64) {
-      dt.template store<false>(zt, kRP, nullptr, 0);
+      dt.store(zf, so);
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = ta[u];
       __syncthreads();
@@ -144,15 +166,15 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
-        const bf16* zr = zt + (16 * wave + c16) * kRP + 32 * c + 4 * g;
-        const bf16x4 zlo = *reinterpret_cast<const bf16x4*>(zr);
-        const bf16x4 zhi = *reinterpret_cast<const bf16x4*>(zr + 16);
-        bf16x8 a8;
+        const int tr = 16 * wave + c16;
+        const float* zr = zf + tr * kSP + so[tr] + 32 * c + 4 * g;
+        float v[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a8[e] = zlo[e];
-          a8[e + 4] = zhi[e];
+          v[e] = zr[e];
+          v[e + 4] = zr[16 + e];
         }
+        const bf16x8 a8 = pack_bf16x8(v);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const bf16x4 blo = lds_tr4(at, kRP, 32 * c + 4 * g, 16 * db, c16);
@@ -201,9 +223,9 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
 
 template <typename GT>
 __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16 zt[64 * kRP];  // [token][s]
-  __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];  // [token][d]
-  __shared__ __attribute__((aligned(16))) float zf[64 * kFP]; // fp32 copy for the plain sums
+  __shared__ __attribute__((aligned(16))) float zf[64 * kSP];  // [token][s + shift]
+  __shared__ __attribute__((aligned(16))) int so[64];
+  __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];   // [token][d]
   __shared__ float bsh[2][64];
   __shared__ float p2red[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
@@ -295,7 +317,7 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&xt[xr * kRP + xc + 8 * u]) = tx[u];
     }
-    if (hit) dt.template store<true>(zt, kRP, zf, kFP);
+    if (hit) dt.store(zf, so);
     if ((has0 || has2) && tid < 64) {
       bsh[0][tid] = tb[0];
       bsh[1][tid] = tb[1];
@@ -309,14 +331,18 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
         // the order 32c + 4g + e, 32c + 16 + 4g + e
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x4 alo = lds_tr4(zt, kRP, 32 * c + 4 * g, 16 * wave, c16);
-          const bf16x4 ahi = lds_tr4(zt, kRP, 32 * c + 16 + 4 * g, 16 * wave, c16);
-          bf16x8 a8;
+          const int sc = 16 * wave + c16;
+          const int t0 = 32 * c + 4 * g;
+          const int4 oa = *reinterpret_cast<const int4*>(&so[t0]);
+          const int4 ob = *reinterpret_cast<const int4*>(&so[t0 + 16]);
+          const int oo[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+          float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            a8[e] = alo[e];
-            a8[e + 4] = ahi[e];
+            v[e] = zf[(t0 + e) * kSP + oo[e] + sc];
+            v[e + 4] = zf[(t0 + 16 + e) * kSP + oo[e + 4] + sc];
           }
+          const bf16x8 a8 = pack_bf16x8(v);
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const bf16x4 blo = lds_tr4(xt, kRP, 32 * c + 4 * g, 16 * db, c16);
@@ -336,7 +362,7 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
         const int s = tid & 63, q = tid >> 6;
         float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part += zf[(16 * q + e) * kFP + s];
+        for (int e = 0; e < 16; ++e) part += zf[(16 * q + e) * kSP + so[16 * q + e] + s];
         p2acc += part;
       }
     }
