@@ -15,7 +15,8 @@
 //   four consecutive keys per 16-key block);
 //   relation terms by tile region: a tile whose offsets delta = i - j all
 //   satisfy delta >= D or delta <= -D is saturated and adds one fp32 entry per
-//   query (folded into the exponent's offset) and one per key; band tiles
+//   query (folded into the exponent's offset) and one per key (the initial
+//   value of the S accumulator); band tiles
 //   read the per-pair projections Z ([RPA] §4.1, App. B saturated-tile lemma).
 //   Every pair with |delta| >= D takes the boundary entries whatever its tile,
 //   exactly as the backward passes do.
@@ -25,7 +26,8 @@
 //   (a factor 256) are O and the row sum rescaled; the result is the same
 //   exact quotient.
 //   O^T += V^T P^T on MFMA with P in registers (bf16, or a bf16 hi + lo pair
-//   under F_SPLIT).
+//   under F_SPLIT); the row sums of P are one more MFMA with a ones operand
+//   (fp32 vector sums under F_SPLIT).
 // The region of each tile is decided per wave from the wave's extreme offsets
 // before the loop (the three ranges of [RPA] §4.3.3).
 #include "relation.hpp"
@@ -40,6 +42,8 @@ constexpr int kWQ = 16 * QB;       // queries per wave
 constexpr int kBM = 4 * kWQ;       // queries per workgroup
 constexpr int kKP = 72;            // K and V tile pitch (bf16): 144-byte rows
 constexpr float kLazy = 8.f;       // rescale threshold, log2 units
+// an MFMA A operand whose 16 rows are all ones (bf16 1.0 = 0x3f80)
+#define kOnes8 (__builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}))
 
 template <int F>
 __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
@@ -195,11 +199,18 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
       const bf16* Vs = sv[buf];
+      // region of the tile for this wave (uniform); on saturated tiles the
+      // key's boundary entry is the initial value of the S accumulator
+      const bool sat = kt < n_hi || kt >= t_lo;
+      const int side = kt < n_hi ? 1 : 0;  // 1: delta >= D (row 2D), 0: delta <= -D
       floatx4 s[QB][4];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int kb = 0; kb < 4; ++kb) {
+        floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (KC && sat) kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = kx;
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -214,19 +225,9 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
       // ---- relation terms: s becomes S plus the per-pair terms (score
       // units); off[qb] is the row's constant term (scaled) on saturated tiles
       float off[QB];
-      if (kt < n_hi || kt >= t_lo) {
-        const int side = kt < n_hi ? 1 : 0;  // 1: delta >= D (row 2D), 0: delta <= -D
+      if (sat) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) off[qb] = (side ? rhi[qb] : rlo[qb]) * sl2;
-        if (KC) {
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const floatx4 kx =
-                *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb] += kx;
-          }
-        }
       } else {
         // band tile: per-pair terms; pairs with |delta| >= D take the
         // boundary entries
@@ -272,6 +273,8 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
         }
       }
       if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > iw)) {
+        // (the empty asm keeps this a branch taken by the edge tiles only)
+        asm volatile("");
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int i = iw + 16 * qb + c16;
@@ -303,19 +306,25 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
           for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
         }
         const float bias = off[qb] - mu[qb];
-        float ls = 0.f;
+        float lv = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const float p = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
             s[qb][kb][t] = p;
-            ls += p;
+            if (SPLIT) lv += p;
           }
-        l[qb] += ls;
+        if (SPLIT) l[qb] += wave_sum_g(lv);
       }
 
-      // ---- O^T += V^T P^T (keys in the permuted order of frag_regs)
+      // ---- O^T += V^T P^T (keys in the permuted order of frag_regs); the
+      // row sums of P come from the same MFMA with a row of ones for V^T, so
+      // they add exactly the bf16 weights that multiply V (with split operands
+      // they are summed in fp32 above: the hi part alone would not match)
+      floatx4 ls[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) ls[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 pf[QB], pl[QB];
@@ -346,6 +355,15 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
               o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], o[qb][db], 0, 0, 0);
           }
         }
+        if (!SPLIT) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[qb], ls[qb], 0, 0, 0);
+        }
+      }
+      if (!SPLIT) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb][0];
       }
     }
 
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float ls = wave_sum_g(l[qb]);
+    const float ls = l[qb];  // the full row sum in every lane of the column
     const int i = iw + 16 * qb + c16;
     if (i >= N) continue;
     const float inv = 1.f / ls;
