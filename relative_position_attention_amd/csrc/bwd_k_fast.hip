@@ -126,40 +126,53 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   float blo[2] = {0.f, 0.f}, bhi[2] = {0.f, 0.f}, csum[2] = {0.f, 0.f};
 
   const int kr = tid >> 3, kc8 = (tid & 7) * 8;
-  uint4 tq, td;
-  float tqs[4] = {0.f, 0.f, 0.f, 0.f};
-  auto load_tile = [&](int i0) {
+  // a query tile in registers on its way to LDS: Q and dO rows (t >> 3), chunk
+  // t & 7, and for t < 32 the query's L (log2 units), D and boundary entries
+  struct TileRegs {
+    uint4 q, d;
+    float s[4];
+  };
+  auto load_tile = [&](TileRegs& r, int i0) {
     const uint32_t off = static_cast<uint32_t>((i0 + kr) * 128 + kc8 * 2);
-    tq = bload16(rq, off);
-    td = bload16(rdo, off);
+    r.q = bload16(rq, off);
+    r.d = bload16(rdo, off);
     if (tid < kT) {
       const int i = i0 + tid;
       const bool ok = i < N;
-      tqs[0] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
-      tqs[1] = ok ? a.dvec[tok + i] : 0.f;
-      tqs[2] = ok ? a.rowlo[tok + i] : 0.f;
-      tqs[3] = ok ? a.rowhi[tok + i] : 0.f;
+      r.s[0] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
+      r.s[1] = ok ? a.dvec[tok + i] : 0.f;
+      r.s[2] = ok ? a.rowlo[tok + i] : 0.f;
+      r.s[3] = ok ? a.rowhi[tok + i] : 0.f;
     }
   };
-  auto store_tile = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sq[buf][kr * kP + kc8]) = tq;
-    *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = td;
+  auto store_tile = [&](const TileRegs& r, int buf) {
+    *reinterpret_cast<uint4*>(&sq[buf][kr * kP + kc8]) = r.q;
+    *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = r.d;
     if (tid < kT) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) sqs[buf][x][tid] = tqs[x];
+      for (int x = 0; x < 4; ++x) sqs[buf][x][tid] = r.s[x];
     }
   };
 
+  // Tiles are loaded two ahead: while tile t is computed from LDS, tile t + 1
+  // is in flight in one register set and tile t + 2 is requested into the
+  // other (the loads of a tile get two tiles' time to arrive).
+  TileRegs ra, rb;
+  ra.s[0] = ra.s[1] = ra.s[2] = ra.s[3] = 0.f;
+  rb.s[0] = rb.s[1] = rb.s[2] = rb.s[3] = 0.f;
   if (it0 < nqt) {
-    load_tile(it0 * kT);
-    store_tile(0);
+    load_tile(ra, it0 * kT);
+    store_tile(ra, 0);
   }
+  if (it0 + 1 < nqt) load_tile(rb, (it0 + 1) * kT);
   __syncthreads();
 
-  for (int it = it0; it < nqt; ++it) {
+  // one tile step: rl held tile it (already in LDS) and now receives tile
+  // it + 2; rs holds tile it + 1, stored to the other LDS buffer at the end
+  auto tile_step = [&](int it, TileRegs& rl, TileRegs& rs) {
     const int buf = (it - it0) & 1;
     const int i0 = it * kT;
-    if (it + 1 < nqt) load_tile(i0 + kT);
+    if (it + 2 < nqt) load_tile(rl, i0 + 2 * kT);
     if (STZQ) {
       // band for some wave of the workgroup: stage Z^Q of the tile's queries
       // for the workgroup's 128 keys, as szq[query][key - j0b]; a query row
@@ -386,8 +399,12 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       }
     }
 
-    if (it + 1 < nqt) store_tile(buf ^ 1);
+    if (it + 1 < nqt) store_tile(rs, buf ^ 1);
     __syncthreads();
+  };
+  for (int it = it0; it < nqt; it += 2) {
+    tile_step(it, ra, rb);
+    if (it + 1 < nqt) tile_step(it + 1, rb, ra);
   }
 
 #pragma unroll
