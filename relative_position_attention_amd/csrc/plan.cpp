@@ -408,6 +408,9 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   int sblocks = (p.S + 63) / 64;
   int subs = p.B * ((p.N + 63) / 64);
   int want = (2048 + sblocks * p.H - 1) / std::max(1, sblocks * p.H);
+  // causal: the offsets near 0 reach every token and the far ones few, so
+  // the longest blocks are split four ways
+  if (p.causal) want = std::max(want, 4);
   p.nchunk = std::max(1, std::min(want, subs));
 
   // ---- z layout (group tables first)

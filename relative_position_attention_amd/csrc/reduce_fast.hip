@@ -121,104 +121,113 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
   const int h = bh % f.H;
-  // widest windows first: under a causal map the last query blocks and the
-  // first key blocks reach the most rows
-  const int rbk = static_cast<int>(blockIdx.x);
-  const int r0 = (f.key_side ? rbk : static_cast<int>(gridDim.x) - 1 - rbk) * 64;
   const int64_t tok = static_cast<int64_t>(bh) * f.N;
-  const int D = f.D;
-  floatx4 acc[4];
+  // one 64-token block: rows r0 .. r0 + 63
+  auto run_block = [&](int r0) {
+    const int D = f.D;
+    floatx4 acc[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const bf16* atab = nullptr;
-  if (f.at != nullptr)
-    atab = reinterpret_cast<const bf16*>(f.at) + static_cast<int64_t>(f.at_shared ? 0 : h) * f.S * 64;
+    for (int db = 0; db < 4; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const bf16* atab = nullptr;
+    if (f.at != nullptr)
+      atab = reinterpret_cast<const bf16*>(f.at) + static_cast<int64_t>(f.at_shared ? 0 : h) * f.S * 64;
 
-  if (f.dz != nullptr && D >= 1) {
-    const int grp = r0 / kGroup;
-    const GroupInfo gi = f.gi[grp];
-    int slo, shi;
-    if (f.key_side)
-      key_group_window(grp, f.N, D, f.causal != 0, slo, shi);
-    else
-      query_group_window(grp, f.N, D, f.causal != 0, slo, shi);
-    const int sa = imax(1, slo), sb = imin(2 * D - 1, shi);
-    const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(f.dz) + static_cast<int64_t>(bh) * f.dz_bh,
-                              static_cast<uint64_t>(f.dz_bh) * sizeof(GT));
-    const Rsrc ra = make_rsrc(atab, static_cast<uint64_t>(f.S) * 128);
-    // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
-    const int ar = tid >> 2, ac = (tid & 3) * 16;
-    DzTile<GT> dt;
-    uint4 ta[2];
-    auto load_stage = [&](int s0) {
-      dt.load(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0);
+    if (f.dz != nullptr && D >= 1) {
+      const int grp = r0 / kGroup;
+      const GroupInfo gi = f.gi[grp];
+      int slo, shi;
+      if (f.key_side)
+        key_group_window(grp, f.N, D, f.causal != 0, slo, shi);
+      else
+        query_group_window(grp, f.N, D, f.causal != 0, slo, shi);
+      const int sa = imax(1, slo), sb = imin(2 * D - 1, shi);
+      const Rsrc rz = make_rsrc(reinterpret_cast<const GT*>(f.dz) + static_cast<int64_t>(bh) * f.dz_bh,
+                                static_cast<uint64_t>(f.dz_bh) * sizeof(GT));
+      const Rsrc ra = make_rsrc(atab, static_cast<uint64_t>(f.S) * 128);
+      // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
+      const int ar = tid >> 2, ac = (tid & 3) * 16;
+      DzTile<GT> dt;
+      uint4 ta[2];
+      auto load_stage = [&](int s0) {
+        dt.load(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        ta[u] = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
-    };
-    if (sa <= sb) load_stage(sa);
-    for (int s0 = sa; s0 <= sb; s0 += 64) {
-      dt.store(zf, so);
+        for (int u = 0; u < 2; ++u)
+          ta[u] = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
+      };
+      if (sa <= sb) load_stage(sa);
+      for (int s0 = sa; s0 <= sb; s0 += 64) {
+        dt.store(zf, so);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = ta[u];
-      __syncthreads();
-      if (s0 + 64 <= sb) load_stage(s0 + 64);
+        for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = ta[u];
+        __syncthreads();
+        if (s0 + 64 <= sb) load_stage(s0 + 64);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
-        const int tr = 16 * wave + c16;
-        const float* zr = zf + tr * kSP + so[tr] + 32 * c + 4 * g;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = zr[e];
-          v[e + 4] = zr[16 + e];
-        }
-        const bf16x8 a8 = pack_bf16x8(v);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x4 blo = lds_tr4(at, kRP, 32 * c + 4 * g, 16 * db, c16);
-          const bf16x4 bhi = lds_tr4(at, kRP, 32 * c + 16 + 4 * g, 16 * db, c16);
-          bf16x8 b8;
+        for (int c = 0; c < 2; ++c) {
+          // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
+          const int tr = 16 * wave + c16;
+          const float* zr = zf + tr * kSP + so[tr] + 32 * c + 4 * g;
+          float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            b8[e] = blo[e];
-            b8[e + 4] = bhi[e];
+            v[e] = zr[e];
+            v[e + 4] = zr[16 + e];
           }
-          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[db], 0, 0, 0);
+          const bf16x8 a8 = pack_bf16x8(v);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x4 blo = lds_tr4(at, kRP, 32 * c + 4 * g, 16 * db, c16);
+            const bf16x4 bhi = lds_tr4(at, kRP, 32 * c + 16 + 4 * g, 16 * db, c16);
+            bf16x8 b8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              b8[e] = blo[e];
+              b8[e + 4] = bhi[e];
+            }
+            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[db], 0, 0, 0);
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
 
-  // epilogue: lane holds rows 16 wave + 4g + t, column 16 db + c16
+    // epilogue: lane holds rows 16 wave + 4g + t, column 16 db + c16
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int i = r0 + 16 * wave + 4 * g + t;
-    if (i >= f.N) continue;
-    const int64_t row = tok + i;
-    float b0 = 0.f, b1 = 0.f, cs = 0.f;
-    if (atab != nullptr && f.bnd != nullptr) {
-      b0 = f.bnd[row * 2 + 0];
-      b1 = f.bnd[row * 2 + 1];
-    }
-    if (f.colsum != nullptr) cs = f.colsum[row];
+    for (int t = 0; t < 4; ++t) {
+      const int i = r0 + 16 * wave + 4 * g + t;
+      if (i >= f.N) continue;
+      const int64_t row = tok + i;
+      float b0 = 0.f, b1 = 0.f, cs = 0.f;
+      if (atab != nullptr && f.bnd != nullptr) {
+        b0 = f.bnd[row * 2 + 0];
+        b1 = f.bnd[row * 2 + 1];
+      }
+      if (f.colsum != nullptr) cs = f.colsum[row];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = 16 * db + c16;
-      float v = acc[db][t] + f.acc[row * 64 + d];
-      if (atab != nullptr)
-        v += b0 * static_cast<float>(atab[d]) + b1 * static_cast<float>(atab[static_cast<int64_t>(2 * D) * 64 + d]);
-      if (f.colsum != nullptr) v += cs * static_cast<float>(reinterpret_cast<const bf16*>(f.u)[h * 64 + d]);
-      if (f.out_f32)
-        reinterpret_cast<float*>(f.out)[row * 64 + d] = v;
-      else
-        reinterpret_cast<bf16*>(f.out)[row * 64 + d] = static_cast<bf16>(v);
+      for (int db = 0; db < 4; ++db) {
+        const int d = 16 * db + c16;
+        float v = acc[db][t] + f.acc[row * 64 + d];
+        if (atab != nullptr)
+          v += b0 * static_cast<float>(atab[d]) + b1 * static_cast<float>(atab[static_cast<int64_t>(2 * D) * 64 + d]);
+        if (f.colsum != nullptr) v += cs * static_cast<float>(reinterpret_cast<const bf16*>(f.u)[h * 64 + d]);
+        if (f.out_f32)
+          reinterpret_cast<float*>(f.out)[row * 64 + d] = v;
+        else
+          reinterpret_cast<bf16*>(f.out)[row * 64 + d] = static_cast<bf16>(v);
+      }
     }
+  };
+  const int nrb = (f.N + 63) / 64;
+  if (f.causal) {
+    // a causal map gives the token blocks windows of linearly growing (query
+    // side) or shrinking (key side) width: each workgroup takes block b and
+    // block nrb - 1 - b, so every workgroup does the same work
+    const int b = static_cast<int>(blockIdx.x);
+    run_block(b * 64);
+    if (nrb - 1 - b != b) run_block((nrb - 1 - b) * 64);
+  } else {
+    run_block(static_cast<int>(blockIdx.x) * 64);
   }
 }
-
 // ---------------------------------------------------------------- partials
 
 template <typename GT>
@@ -424,7 +433,8 @@ inline unsigned nblk(int64_t n, int b) { return static_cast<unsigned>((n + b - 1
 }  // namespace
 
 hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s) {
-  dim3 grid(nblk(f.N, 64), BH);
+  const unsigned nrb = nblk(f.N, 64);
+  dim3 grid(f.causal ? (nrb + 1) / 2 : nrb, BH);
   if (f.dz_f32)
     hipLaunchKernelGGL((finalize_fast<float>), grid, dim3(256), 0, s, f);
   else
