@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[2][3][64 * P];  // K rows, K^T, V rows
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
   const int nqb = (N + 127) / 128;
   const int qblk = CAUSAL ? (nqb - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * P];  // Q rows, Q^T, dO rows, dO^T
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
   const int bh = blockIdx.y;
   const int h = bh % a.H;

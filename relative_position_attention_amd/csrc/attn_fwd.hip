@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T lds[2][2][64 * P];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
   const int nqb = (N + 127) / 128;
   const int qblk = CAUSAL ? (nqb - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);

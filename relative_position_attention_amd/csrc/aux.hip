@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void project_kernel(ProjectArgs p) {
   using Frag = typename M::frag;
   using ZT = typename Store<T>::Z;
   constexpr int E = M::E, KS = M::KS, NST = 64 / KS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.z;
   const int h = bh % p.H;
   const int r0 = blockIdx.y * 64;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs f) {
   constexpr int E = M::E, KS = M::KS, KC = RedP<T>::KC, LP = RedP<T>::P;
   __shared__ __attribute__((aligned(16))) T zs[64 * LP];
   __shared__ __attribute__((aligned(16))) T as[64 * LP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
   const int h = bh % f.H;
   const int r0 = blockIdx.x * 64;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void partials_kernel(PartialArgs p) {
   __shared__ __attribute__((aligned(16))) float zt[64 * ZP];  // [s][token]
   __shared__ __attribute__((aligned(16))) T xt[64 * P];       // [d][token]
   __shared__ float bsh[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int s0 = blockIdx.x * 64;
   const int h = blockIdx.y;
   const int chunk = blockIdx.z;

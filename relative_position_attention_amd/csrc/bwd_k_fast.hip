@@ -38,6 +38,8 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   // query projections of a band tile are staged into LDS once per workgroup
   constexpr bool STZQ = (F & F_ZQ) != 0;
+  // causal masks: pair each 16-key block with its mirror (below)
+  constexpr bool PAIR = CAUSAL && !(F & F_ZK) && !DZ;
   constexpr int kZP = 136;  // szq pitch (fp16)
   __shared__ __attribute__((aligned(16))) _Float16 szq[STZQ ? kT * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sq[2][kT * kP];
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   __shared__ __attribute__((aligned(16))) float sqs[2][4][kT];  // l2, D, rowlo, rowhi
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
 
   int item = static_cast<int>(blockIdx.x);
@@ -66,8 +68,36 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   }
   const int h = bh % a.H;
   const int64_t tok = static_cast<int64_t>(bh) * N;
-  const int j0b = kblk * 128;
-  const int jw = j0b + 32 * wave;
+  // The wave's keys: two blocks of 16 starting at jbase[0], jbase[1]; jloc is
+  // their column in the staged Z^Q rows.  Without PAIR the workgroup owns 128
+  // consecutive keys (one projection group).  With PAIR (causal masks) wave w
+  // of workgroup m owns 16-key block kH = 4m + w and its mirror
+  // kL = n16 - 1 - kH: a key is seen by the queries at or after it, so every
+  // wave then has the same work (a lone middle block is taken as block 0).
+  // The staged key ranges are then [64m, 64m + 64) and the 64 keys ending
+  // with block n16 - 1 - 4m.
+  int jbase[2], jloc[2];
+  bool kon[2];
+  int j0b, jrB = 0;
+  if (PAIR) {
+    const int n16 = (N + 15) / 16;
+    const int kH = 4 * kblk + wave, kL = n16 - 1 - kH;
+    jbase[0] = 16 * kH;
+    jbase[1] = 16 * kL;
+    kon[0] = kH <= kL;
+    kon[1] = kH < kL;
+    j0b = 64 * kblk;
+    jrB = 16 * (n16 - 4 - 4 * kblk);
+    jloc[0] = 16 * wave;
+    jloc[1] = 64 + 16 * (3 - wave);
+  } else {
+    j0b = kblk * 128;
+    jbase[0] = j0b + 32 * wave;
+    jbase[1] = jbase[0] + 16;
+    kon[0] = kon[1] = true;
+    jloc[0] = 32 * wave;
+    jloc[1] = 32 * wave + 16;
+  }
   const float sl2 = a.scale_log2, tau = a.scale;
   const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
   const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
@@ -75,24 +105,25 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
   const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
 
-  // keys of this lane: jw + 16 kb + c16
+  // keys of this lane: jbase[kb] + c16
   bf16x8 kf[2][2], vf[2][2];
   float klo[2], khi[2], kmid[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int j = jw + 16 * kb + c16;
+    const int j = jbase[kb] + c16;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint32_t off = static_cast<uint32_t>(j * 128 + 64 * c + 16 * g);
       kf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rk, off));
       vf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rv, off));
     }
-    const bool ok = j < N;
+    const bool ok = j < N && kon[kb];
     klo[kb] = (KC && ok) ? a.keylo[tok + j] : 0.f;
     khi[kb] = (KC && ok) ? a.keyhi[tok + j] : 0.f;
     kmid[kb] = (KC && ok) ? a.keymid[tok + j] : 0.f;
   }
   GroupInfo gik = {0, 0, 0, 0};
+  const int gk0 = (j0b / kGroup) * kGroup;  // (used without PAIR only)
   if ((F & F_ZK) || DZ) gik = a.gk[j0b / kGroup];
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
@@ -103,17 +134,23 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
 
-  // query tiles: causal starts at the block's first key; the wave's tiles
+  // query tiles: causal starts at the workgroup's first key; a block's tiles
   // before its own first key are fully masked and skipped.  Regions from the
-  // wave's extreme offsets: [it_first, n_lo) all delta <= -D, [t_hi, nqt) all
-  // delta >= D.
+  // block's extreme offsets: [itk, n_lo) all delta <= -D, [t_hi, nqt) all
+  // delta >= D (without PAIR both blocks use the wave's 32-key range).
   const int nqt = (N + kT - 1) / kT;
   const int it0 = CAUSAL ? j0b / kT : 0;
-  const int itw = CAUSAL ? jw / kT : 0;
-  int n_lo = (jw - D - (kT - 1) >= 0) ? (jw - D - (kT - 1)) / kT + 1 : 0;
-  n_lo = CAUSAL ? itw : imax(itw, imin(n_lo, nqt));
-  int t_hi = (jw + 31 + D + kT - 1) / kT;
-  t_hi = imax(n_lo, imin(t_hi, nqt));
+  int itk[2], n_lo[2], t_hi[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int ja = jbase[PAIR ? kb : 0], jz = jbase[PAIR ? kb : 1] + 15;
+    itk[kb] = !kon[kb] ? nqt : (CAUSAL ? ja / kT : 0);
+    int nl = (ja - D - (kT - 1) >= 0) ? (ja - D - (kT - 1)) / kT + 1 : 0;
+    n_lo[kb] = CAUSAL ? itk[kb] : imax(itk[kb], imin(nl, nqt));
+    const int th = (jz + D + kT - 1) / kT;
+    t_hi[kb] = imax(n_lo[kb], imin(th, nqt));
+  }
+  const int itw = itk[0];  // block 0 starts first (PAIR: the earlier keys)
 
   floatx4 dk[2][4], dv[2][4];
 #pragma unroll
@@ -175,28 +212,33 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     if (it + 2 < nqt) load_tile(rl, i0 + 2 * kT);
     if (STZQ) {
       // band for some wave of the workgroup: stage Z^Q of the tile's queries
-      // for the workgroup's 128 keys, as szq[query][key - j0b]; a query row
-      // holds them as 128 consecutive entries in descending key order from a
-      // 16-byte boundary (the query-side pad), so each chunk is reversed
-      const bool blk_sat = (i0 - (j0b + 127) >= D) || (i0 + kT - 1 - j0b <= -D);
-      if (!blk_sat) {
+      // for the workgroup's keys, as szq[query][key column]; a query row holds
+      // 64 consecutive keys in descending order from a 16-byte boundary (the
+      // query-side pad), so each chunk is reversed.  Columns 0..63 are keys
+      // j0b.., 64..127 keys j0b + 64.. (PAIR: keys jrB..).
+      const int jr0 = j0b, jr1 = PAIR ? jrB : j0b + 64;
+      const bool sat0 = (i0 - (jr0 + 63) >= D) || (i0 + kT - 1 - jr0 <= -D);
+      const bool sat1 = (i0 - (jr1 + 63) >= D) || (i0 + kT - 1 - jr1 <= -D);
+      if (!(sat0 && sat1)) {
         const GroupInfo gq = a.gq[i0 / kGroup];
         const int gq0s = (i0 / kGroup) * kGroup;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int idx = tid + 256 * u;
           const int r = idx >> 4, ch = idx & 15;
+          const int half = ch >> 3, chl = ch & 7;
+          const int jtop = (half ? jr1 : jr0) + 63;
           const int i = i0 + r;
-          const int col = (i - (j0b + 127) + D) - gq.slo + gq.pad + 8 * ch;
+          const int col = (i - jtop + D) - gq.slo + gq.pad + 8 * chl;
           const int e = gq.base + (i - gq0s) * gq.pitch + col;
           const uint4 w = bload16(rzq, (i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
-          // entries 8 ch .. 8 ch + 7 of the run are keys j0b + 127 - 8 ch - (0..7)
+          // entries 8 chl .. 8 chl + 7 of the run are keys jtop - 8 chl - (0..7)
           uint4 rev;
           rev.x = __builtin_amdgcn_perm(w.w, w.w, 0x01000302u);
           rev.y = __builtin_amdgcn_perm(w.z, w.z, 0x01000302u);
           rev.z = __builtin_amdgcn_perm(w.y, w.y, 0x01000302u);
           rev.w = __builtin_amdgcn_perm(w.x, w.x, 0x01000302u);
-          *reinterpret_cast<uint4*>(szq + r * kZP + (120 - 8 * ch)) = rev;
+          *reinterpret_cast<uint4*>(szq + r * kZP + (64 * half + 56 - 8 * chl)) = rev;
         }
         __syncthreads();
       }
@@ -205,13 +247,21 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     if (it >= itw) {
       const bf16* Qs = sq[buf];
       const bf16* Ds = sd[buf];
-      // region of the tile for this wave (uniform); on saturated tiles the
-      // key's boundary entry is the initial value of the S accumulator
-      const bool sat_lo = it < n_lo, sat_hi = it >= t_hi;
+      // per block (uniform): does the tile reach it, and its region; on
+      // saturated tiles the key's boundary entry is the initial value of the
+      // S accumulator.  A block the tile does not reach is block 1 (block 0
+      // starts first), so block 0's products are always made.
+      bool sat_lo[2], sat_hi[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sat_lo[kb] = it < n_lo[kb];
+        sat_hi[kb] = it >= t_hi[kb];
+      }
+      const bool both = PAIR ? it >= itk[1] : true;
       floatx4 s[2][2], dp[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float k0 = (KC && (sat_lo || sat_hi)) ? (sat_hi ? khi[kb] : klo[kb]) : 0.f;
+        const float k0 = (KC && (sat_lo[kb] || sat_hi[kb])) ? (sat_hi[kb] ? khi[kb] : klo[kb]) : 0.f;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           s[qb][kb] = floatx4{k0, k0, k0, k0};
@@ -224,15 +274,20 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         for (int qb = 0; qb < 2; ++qb) {
           const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + c16) * kP + 32 * c + 8 * g);
           const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + (16 * qb + c16) * kP + 32 * c + 8 * g);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kb][c], s[qb][kb], 0, 0, 0);
-            dp[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[kb][c], dp[qb][kb], 0, 0, 0);
+          s[qb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[0][c], s[qb][0], 0, 0, 0);
+          dp[qb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[0][c], dp[qb][0], 0, 0, 0);
+          if (both) {
+            s[qb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[1][c], s[qb][1], 0, 0, 0);
+            dp[qb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[1][c], dp[qb][1], 0, 0, 0);
           }
         }
       }
 
-      const bool need_mask = (i0 + kT > N) || (jw + 32 > N) || (CAUSAL && i0 < jw + 31);
+      bool need_mask[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        need_mask[kb] = (i0 + kT > N) || (jbase[PAIR ? kb : 1] + 16 > N) ||
+                        (CAUSAL && i0 < jbase[PAIR ? kb : 1] + 15);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int i1 = i0 + 16 * qb + 4 * g;
@@ -240,12 +295,13 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         const floatx4 ql2 = *reinterpret_cast<const floatx4*>(&sqs[buf][0][qo]);
         const floatx4 qrl = *reinterpret_cast<const floatx4*>(&sqs[buf][2][qo]);
         const floatx4 qrh = *reinterpret_cast<const floatx4*>(&sqs[buf][3][qo]);
-        if (sat_lo || sat_hi) {
-          // saturated tile: the query's entry and L fold into one offset per
-          // query (the key's entry is already in the accumulator)
+        if (!PAIR && (sat_lo[0] || sat_hi[0])) {
+          // saturated tile (both blocks): the query's entry and L fold into
+          // one offset per query (the key's entry is already in the
+          // accumulator)
           float cq[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) cq[t] = fmaf(sat_hi ? qrh[t] : qrl[t], sl2, -ql2[t]);
+          for (int t = 0; t < 4; ++t) cq[t] = fmaf(sat_hi[0] ? qrh[t] : qrl[t], sl2, -ql2[t]);
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -254,14 +310,25 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int j = jw + 16 * kb + c16;
+          if (kb == 1 && !both) continue;
+          if (PAIR && (sat_lo[kb] || sat_hi[kb])) {
+            // saturated tile: the query's entry and L fold into one offset
+            // per query (the key's entry is already in the accumulator)
+            float cq[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) cq[t] = fmaf(sat_hi[kb] ? qrh[t] : qrl[t], sl2, -ql2[t]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t], sl2, cq[t]));
+            continue;
+          }
+          const int j = jbase[kb] + c16;
           float rel[4];
           {
             float zk[4] = {0.f, 0.f, 0.f, 0.f};
             if (F & F_ZK) {
               const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
               const uint32_t offk = j < N
-                  ? static_cast<uint32_t>((gik.base + (j - j0b) * gik.pitch + c0) * 2) : kOob;
+                  ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + c0) * 2) : kOob;
               const halfx4 hv = __builtin_bit_cast(halfx4, bload8(rzk, offk));
 #pragma unroll
               for (int t = 0; t < 4; ++t) zk[t] = static_cast<float>(hv[t]);  // ascending
@@ -269,7 +336,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
             halfx4 zq4 = halfx4{0, 0, 0, 0};
             if (STZQ)  // Z^Q[i1 + t][i1 + t - j + D], t = 0..3
               zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq), kZP,
-                                                       16 * qb + 4 * g, 32 * wave + 16 * kb, c16));
+                                                       16 * qb + 4 * g, jloc[kb], c16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int i = i1 + t;
@@ -284,21 +351,26 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
           for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t] + rel[t], sl2, -ql2[t]));
         }
       }
-      if (need_mask) {
-        // (the empty asm keeps this a branch: without it the compiler turns
-        // the rare masked pass into selects on every tile)
-        asm volatile("");
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 1 && (!PAIR || !both)) continue;
+        if (need_mask[kb]) {
+          // (the empty asm keeps this a branch: without it the compiler turns
+          // the rare masked pass into selects on every tile)
+          asm volatile("");
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const int j = jw + 16 * kb + c16;
+          for (int kx = 0; kx < 2; ++kx) {
+            if (PAIR && kx != kb) continue;  // without PAIR one pass masks both blocks
+            const int j = jbase[kx] + c16;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int i = i0 + 16 * qb + 4 * g + t;
-              if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = 0.f;
-            }
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int i = i0 + 16 * qb + 4 * g + t;
+                if (j >= N || (CAUSAL && j > i)) s[qb][kx][t] = 0.f;
+              }
           }
+        }
       }
       // G' = P (dP - D)
 #pragma unroll
@@ -314,16 +386,17 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       if (DZ || CS) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int j = jw + 16 * kb + c16;
+          if (kb == 1 && !both) continue;
+          const int j = jbase[kb] + c16;
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) {
             const int i1 = i0 + 16 * qb + 4 * g;
             const float gs = (dp[qb][kb][0] + dp[qb][kb][1]) + (dp[qb][kb][2] + dp[qb][kb][3]);
             if (CS) csum[kb] += gs;
             if (DZ) {
-              if (sat_lo) {
+              if (sat_lo[kb]) {
                 blo[kb] += gs;
-              } else if (sat_hi) {
+              } else if (sat_hi[kb]) {
                 bhi[kb] += gs;
               } else {
                 float run[4];
@@ -346,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
                 }
                 if (any) {
                   bf16* row = reinterpret_cast<bf16*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh +
-                              gik.base + static_cast<int64_t>(j - j0b) * gik.pitch;
+                              gik.base + static_cast<int64_t>(j - gk0) * gik.pitch;
                   store4(row + ((i1 - j + D) - gik.slo + gik.pad), run);
                 }
               }
@@ -388,6 +461,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
           }
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
+            if (kb == 1 && !both) continue;
             dv[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt8, pf[kb], dv[kb][db], 0, 0, 0);
             dk[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt8, gf[kb], dk[kb][db], 0, 0, 0);
             if (SPLIT) {
@@ -409,11 +483,11 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int j = jw + 16 * kb + c16;
+    const int j = jbase[kb] + c16;
     const float lo = tau * wave_sum_g(blo[kb]);
     const float hi = tau * wave_sum_g(bhi[kb]);
     const float cs = tau * wave_sum_g(csum[kb]);
-    if (j >= N) continue;
+    if (j >= N || !kon[kb]) continue;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       float dvv[4] = {dv[kb][db][0], dv[kb][db][1], dv[kb][db][2], dv[kb][db][3]};
@@ -434,7 +508,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
 template <int F>
 hipError_t launch_kf(const AttnArgs& a, int B, hipStream_t s) {
-  const int nkb = (a.N + 127) / 128;
+  constexpr bool PAIR = (F & F_CAUSAL) && !(F & F_ZK) && !(F & F_DZK);
+  // PAIR: workgroup m owns 16-key blocks 4m .. 4m+3 and their mirrors
+  const int n16 = (a.N + 15) / 16;
+  const int nkb = PAIR ? ((n16 + 1) / 2 + 3) / 4 : (a.N + 127) / 128;
   const int total = nkb * B * a.H;
   const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
   hipLaunchKernelGGL((bwd_k_fast<F>), dim3(total), dim3(256), 0, s, a, nkb, total, xcd_map);

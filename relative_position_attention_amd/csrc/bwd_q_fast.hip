@@ -36,6 +36,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   using GT = typename DzType<bf16, (F & F_DZ32) != 0>::type;
   // key projections of a band tile are staged into LDS once per workgroup
   constexpr bool STZK = (F & F_ZK) != 0;
+  // causal masks: pair each 16-query block with its mirror (below)
+  constexpr bool PAIR = CAUSAL && !STZK;
   constexpr int kZP = 136;  // szk pitch (fp16)
   __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kP];
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
 
   int item = static_cast<int>(blockIdx.x);
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   const int BH = total / nqb;
   int bh, qblk;
   if (CAUSAL) {
-    qblk = nqb - 1 - item / BH;
+    qblk = item / BH;
     bh = item % BH;
   } else {
     bh = item / nqb;
@@ -63,8 +65,6 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   }
   const int h = bh % a.H;
   const int64_t tok = static_cast<int64_t>(bh) * N;
-  const int i0 = qblk * 128;
-  const int iw = i0 + 32 * wave;
   const float sl2 = a.scale_log2, tau = a.scale;
   const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
   const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
@@ -72,25 +72,68 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
   const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
 
+  // The wave's queries: two blocks of 16 starting at qbase[0], qbase[1].
+  // Without PAIR they are consecutive (the workgroup owns 128 consecutive
+  // queries, one projection group).  With PAIR (causal masks) wave w of
+  // workgroup m owns 16-query block kL = 4m + w and its mirror
+  // kH = n16 - 1 - kL: a causal block reaches keys up to its own position,
+  // so every wave then has the same work, kL + kH + 2 key blocks of 16
+  // (a lone middle block is taken as block 1).
+  int qbase[2];
+  bool qon[2];
+  int i0;  // first query of the workgroup's key-tile range owner (non-PAIR)
+  int nkt;
+  if (PAIR) {
+    const int n16 = (N + 15) / 16;
+    const int kL = 4 * qblk + wave, kH = n16 - 1 - kL;
+    qbase[0] = 16 * kL;
+    qbase[1] = 16 * kH;
+    qon[0] = kL < kH;
+    qon[1] = kL <= kH;
+    i0 = 0;
+    // the workgroup's widest block is wave 0's mirror
+    const int kH0 = n16 - 1 - 4 * qblk;
+    nkt = imin(N - 1, 16 * kH0 + 15) / 64 + 1;
+  } else {
+    i0 = qblk * 128;
+    qbase[0] = i0 + 32 * wave;
+    qbase[1] = qbase[0] + 16;
+    qon[0] = qon[1] = true;
+    const int ilast_b = imin(N - 1, i0 + 127);
+    nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
+  }
+
   bf16x8 qf[2][2], df[2][2];
   float rlo[2], rhi[2], l2[2], dd[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int i = iw + 16 * qb + c16;
+    const int i = qbase[qb] + c16;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const uint32_t off = static_cast<uint32_t>(i * 128 + 64 * c + 16 * g);
       qf[qb][c] = __builtin_bit_cast(bf16x8, bload16(rq, off));
       df[qb][c] = __builtin_bit_cast(bf16x8, bload16(rdo, off));
     }
-    const bool ok = i < N;
+    const bool ok = i < N && qon[qb];
     rlo[qb] = ok ? a.rowlo[tok + i] : 0.f;
     rhi[qb] = ok ? a.rowhi[tok + i] : 0.f;
     l2[qb] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
     dd[qb] = ok ? a.dvec[tok + i] : 0.f;
   }
-  GroupInfo giq = {0, 0, 0, 0};
-  if ((F & F_ZQ) || DZ) giq = a.gq[i0 / kGroup];
+  // projection group of each block (a 16-query block lies in one group)
+  GroupInfo giq[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  int gq0[2];
+  if (PAIR) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      gq0[qb] = (qbase[qb] / kGroup) * kGroup;
+      if (((F & F_ZQ) || DZ) && qon[qb]) giq[qb] = a.gq[qbase[qb] / kGroup];
+    }
+  } else {
+    // both blocks in the workgroup's group
+    gq0[0] = gq0[1] = i0;
+    if ((F & F_ZQ) || DZ) giq[0] = giq[1] = a.gq[i0 / kGroup];
+  }
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
     rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,
@@ -99,15 +142,22 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
-  GT* dzbase = DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh + giq.base : nullptr;
+  GT* dzslice = DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh : nullptr;
 
-  const int ilast_b = imin(N - 1, i0 + 127);
-  const int nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
-  const int nkt_w = CAUSAL ? imin(nkt, (iw + 31) / 64 + 1) : nkt;
-  int n_hi = (iw - D - 63 >= 0) ? (iw - D - 63) / 64 + 1 : 0;
-  n_hi = imin(n_hi, nkt_w);
-  int t_lo = CAUSAL ? nkt_w : (iw + 31 + D + 63) / 64;
-  t_lo = imax(n_hi, imin(t_lo, nkt_w));
+  // key-tile ranges of each block: tiles [0, nkq) are visible; [0, n_hi) have
+  // delta >= D for every pair of the block, [t_lo, nkq) delta <= -D
+  // (without PAIR the two blocks share the wave's 32-query ranges)
+  int nkq[2], n_hi[2], t_lo[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qa = qbase[PAIR ? qb : 0], qz = qbase[PAIR ? qb : 1] + 15;
+    nkq[qb] = !qon[qb] ? 0 : (CAUSAL ? imin(nkt, imin(N - 1, qz) / 64 + 1) : nkt);
+    int nh = (qa - D - 63 >= 0) ? (qa - D - 63) / 64 + 1 : 0;
+    n_hi[qb] = imin(nh, nkq[qb]);
+    const int tl = CAUSAL ? nkq[qb] : (qz + D + 63) / 64;
+    t_lo[qb] = imax(n_hi[qb], imin(tl, nkq[qb]));
+  }
+  const int nkt_w = imax(nkq[0], nkq[1]);
 
   floatx4 dq[2][4];
 #pragma unroll
@@ -173,18 +223,28 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
       const bf16* Vs = sv[buf];
-      // region of the tile for this wave (uniform): saturated tiles take one
-      // entry per query (off) and one per key, the latter as the initial
-      // value of the S accumulator
-      const bool sat = kt < n_hi || kt >= t_lo;
-      const int side = kt < n_hi ? 1 : 0;
+      // per block (uniform): does the tile reach it, and its region; on
+      // saturated tiles the key's entry is the initial value of the S
+      // accumulator and the query's entry goes into off
+      bool act[2], sat[2];
+      int side[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        act[qb] = PAIR ? kt < nkq[qb] : true;
+        sat[qb] = kt < n_hi[qb] || kt >= t_lo[qb];
+        side[qb] = kt < n_hi[qb] ? 1 : 0;
+      }
+      // a block that the tile does not reach is always block 0 (block 1 is
+      // the wider one), so block 1's products are always made
+      const bool both = act[0];
       floatx4 s[2][4], dp[2][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (KC && sat) kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+          floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (KC && sat[qb])
+            kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
           s[qb][kb] = kx;
           dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
@@ -195,82 +255,84 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kP + 32 * c + 8 * g);
           const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (16 * kb + c16) * kP + 32 * c + 8 * g);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
-            dp[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[qb][c], dp[qb][kb], 0, 0, 0);
+          if (both) {
+            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][c], s[0][kb], 0, 0, 0);
+            dp[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[0][c], dp[0][kb], 0, 0, 0);
           }
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][c], s[1][kb], 0, 0, 0);
+          dp[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[1][c], dp[1][kb], 0, 0, 0);
         }
       }
 
       // relation terms (same values as the forward); off = the row's
       // constant on saturated tiles
       float off[2];
-      if (sat) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) off[qb] = side ? rhi[qb] : rlo[qb];
-      } else {
+      for (int qb = 0; qb < 2; ++qb) {
+        off[qb] = 0.f;
+        if (!act[qb]) continue;
+        if (sat[qb]) {
+          off[qb] = side[qb] ? rhi[qb] : rlo[qb];
+          continue;
+        }
+        const int i = qbase[qb] + c16;
+        const bool iok = i < N;
+        const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          off[qb] = 0.f;
-          const int i = iw + 16 * qb + c16;
-          const bool iok = i < N;
-          const int zrow = giq.base + (i - i0) * giq.pitch;
+        for (int kb = 0; kb < 4; ++kb) {
+          const int j1 = j0 + 16 * kb + 4 * g;
+          float zq[4] = {0.f, 0.f, 0.f, 0.f};
+          if (F & F_ZQ) {
+            const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+            const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            const halfx4 hv = __builtin_bit_cast(halfx4, w);
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const int j1 = j0 + 16 * kb + 4 * g;
-            float zq[4] = {0.f, 0.f, 0.f, 0.f};
-            if (F & F_ZQ) {
-              const int c0 = clamp_run((i - (j1 + 3) + D) - giq.slo + giq.pad, giq.pitch);
-              const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
-              const halfx4 hv = __builtin_bit_cast(halfx4, w);
-#pragma unroll
-              for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);
-            }
-            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
-            if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
-            if (KC3) {
-              klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
-              khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
-            }
-            halfx4 zk4 = halfx4{0, 0, 0, 0};
-            if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
-              zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
-                                                       16 * kb + 4 * g, 32 * wave + 16 * qb, c16));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int j = j1 + t;
-              const int dl = i - j;
-              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
-              float band = km[t] + zq[t];
-              if (F & F_ZK) band += static_cast<float>(zk4[t]);
-              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
-            }
-            // keep each 4-run's loads next to their use (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);
           }
+          floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
+          if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+          if (KC3) {
+            klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
+            khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
+          }
+          halfx4 zk4 = halfx4{0, 0, 0, 0};
+          if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
+            zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
+                                                     16 * kb + 4 * g, qbase[qb] - i0, c16));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int j = j1 + t;
+            const int dl = i - j;
+            const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
+            float band = km[t] + zq[t];
+            if (F & F_ZK) band += static_cast<float>(zk4[t]);
+            if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+            s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+          }
+          // keep each 4-run's loads next to their use (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw);
 
       // P, then G' = P (dP - D) in place of s; tau is applied to the sums
       // of G' (dQ, the boundary sums) and to the band entries as written
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        if (!act[qb]) continue;
         const float bias = off[qb] * sl2 - l2[qb];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
       }
-      if (need_mask) {
-        // (the empty asm keeps this a branch: without it the compiler turns
-        // the rare masked pass into selects on every tile)
-        asm volatile("");
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int i = iw + 16 * qb + c16;
+      for (int qb = 0; qb < 2; ++qb) {
+        if (!act[qb]) continue;
+        if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > qbase[qb])) {
+          // (the empty asm keeps this a branch: without it the compiler turns
+          // the rare masked pass into selects on every tile)
+          asm volatile("");
+          const int i = qbase[qb] + c16;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -281,61 +343,59 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         }
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
+        if (!act[qb]) continue;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int t = 0; t < 4; ++t) s[qb][kb][t] *= dp[qb][kb][t] - dd[qb];
+      }
 
       // offset gradients of the queries
       if (DZ) {
-        if (sat) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!act[qb]) continue;
+          if (sat[qb]) {
             float acc = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
               acc += (s[qb][kb][0] + s[qb][kb][1]) + (s[qb][kb][2] + s[qb][kb][3]);
-            if (side)
+            if (side[qb])
               bhi[qb] += acc;
             else
               blo[qb] += acc;
+            continue;
           }
-        } else {
+          const int i = qbase[qb] + c16;
+          GT* rowp = dzslice + giq[qb].base + static_cast<int64_t>(i - gq0[qb]) * giq[qb].pitch;
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int i = iw + 16 * qb + c16;
+          for (int kb = 0; kb < 4; ++kb) {
+            const int j1 = j0 + 16 * kb + 4 * g;
+            float run[4];
+            bool any = false;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const int j1 = j0 + 16 * kb + 4 * g;
-              float run[4];
-              bool any = false;
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const int j = j1 + t;
-                const int dl = i - j;
-                const float gg = s[qb][kb][t];
-                float bandv = 0.f;  // tau G' for the band entry
-                if (dl >= D)
-                  bhi[qb] += gg;
-                else if (dl <= -D)
-                  blo[qb] += gg;
-                else {
-                  bandv = tau * gg;
-                  any = any || (i < N && j < N && (!CAUSAL || j <= i));
-                }
-                run[3 - t] = bandv;  // descending columns
+            for (int t = 0; t < 4; ++t) {
+              const int j = j1 + t;
+              const int dl = i - j;
+              const float gg = s[qb][kb][t];
+              float bandv = 0.f;  // tau G' for the band entry
+              if (dl >= D)
+                bhi[qb] += gg;
+              else if (dl <= -D)
+                blo[qb] += gg;
+              else {
+                bandv = tau * gg;
+                any = any || (i < N && j < N && (!CAUSAL || j <= i));
               }
-              if (any) {
-                GT* row = dzbase + static_cast<int64_t>(i - i0) * giq.pitch;
-                store4(row + ((i - (j1 + 3) + D) - giq.slo + giq.pad), run);
-              }
+              run[3 - t] = bandv;  // descending columns
             }
+            if (any) store4(rowp + ((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad), run);
           }
         }
       }
 
-      // dQ^T += K^T G^T
+      // dQ^T += K^T G'^T
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 gf[2], gl[2];
@@ -357,12 +417,14 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
             kt8[e] = lo[e];
             kt8[e + 4] = hi[e];
           }
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            dq[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gf[qb], dq[qb][db], 0, 0, 0);
+          if (both) {
+            dq[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gf[0], dq[0][db], 0, 0, 0);
             if (SPLIT)
-              dq[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gl[qb], dq[qb][db], 0, 0, 0);
+              dq[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gl[0], dq[0][db], 0, 0, 0);
           }
+          dq[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gf[1], dq[1][db], 0, 0, 0);
+          if (SPLIT)
+            dq[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt8, gl[1], dq[1][db], 0, 0, 0);
         }
       }
     }
@@ -373,10 +435,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int i = iw + 16 * qb + c16;
+    const int i = qbase[qb] + c16;
     const float lo = tau * wave_sum_g(blo[qb]);
     const float hi = tau * wave_sum_g(bhi[qb]);
-    if (i >= N) continue;
+    if (i >= N || !qon[qb]) continue;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       float vals[4] = {tau * dq[qb][db][0], tau * dq[qb][db][1], tau * dq[qb][db][2],
@@ -392,7 +454,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 
 template <int F>
 hipError_t launch_qf(const AttnArgs& a, int B, hipStream_t s) {
-  const int nqb = (a.N + 127) / 128;
+  constexpr bool PAIR = (F & F_CAUSAL) && !(F & F_ZK);
+  // PAIR: workgroup m owns 16-query blocks 4m .. 4m+3 and their mirrors
+  const int n16 = (a.N + 15) / 16;
+  const int nqb = PAIR ? ((n16 + 1) / 2 + 3) / 4 : (a.N + 127) / 128;
   const int total = nqb * B * a.H;
   const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
   hipLaunchKernelGGL((bwd_q_fast<F>), dim3(total), dim3(256), 0, s, a, nqb, total, xcd_map);

@@ -187,6 +187,15 @@ __device__ __forceinline__ bf16x4 lds_tr4(const bf16* tile, int pitch, int row0,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: everything derived from it stays in scalar registers, so branches on
+// it are scalar branches.  (Derived from the lane id alone, the compiler
+// treats it as varying per lane and turns such branches into EXEC-masked
+// regions, which must not hold matrix instructions.)
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // ---- buffer resources: 32-bit offsets, loads past `bytes` return zero (the
 // hardware range check replaces per-lane bounds branches)
 typedef __amdgpu_buffer_rsrc_t Rsrc;

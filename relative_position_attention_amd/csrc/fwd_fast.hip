@@ -46,7 +46,7 @@ constexpr float kLazy = 8.f;       // rescale threshold, log2 units
 #define kOnes8 (__builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}))
 
 template <int F>
-__global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
+__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
                                                           int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
@@ -57,6 +57,8 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
   constexpr bool KC3 = (F & F_ZK) != 0;
   // key projections of a band tile are staged into LDS once per workgroup
   constexpr bool STZK = (F & F_ZK) != 0;
+  // causal masks: pair each 16-query block with its mirror (below)
+  constexpr bool PAIR = CAUSAL && !STZK;
   constexpr int kZP = 136;  // szk pitch (fp16)
   __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int N = a.N, D = a.D;
 
   // Work item.  Non-causal: items are head-major and, with xcd_map, each of
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
   const int BH = total / nqb;
   int bh, qblk;
   if (CAUSAL) {
-    qblk = nqb - 1 - item / BH;
+    qblk = PAIR ? item / BH : nqb - 1 - item / BH;
     bh = item % BH;
   } else {
     bh = item / nqb;
@@ -88,30 +90,66 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
   }
   const int h = bh % a.H;
   const int64_t tok = static_cast<int64_t>(bh) * N;
-  const int i0 = qblk * kBM;
-  const int iw = i0 + kWQ * wave;
+  // The wave's queries: QB blocks of 16 starting at qbase[qb].  Without PAIR
+  // they are consecutive (the workgroup owns kBM consecutive queries).  With
+  // PAIR (causal masks) wave w of workgroup m owns 16-query block
+  // kL = 4m + w and its mirror kH = n16 - 1 - kL: a causal block reaches keys
+  // up to its own position, so every wave then has the same work (a lone
+  // middle block is taken as block 1).
+  static_assert(!PAIR || QB == 2, "pairing takes two 16-query blocks per wave");
+  int qbase[QB];
+  bool qon[QB];
+  int i0, nkt;
+  if (PAIR) {
+    const int n16 = (N + 15) / 16;
+    const int kL = 4 * qblk + wave, kH = n16 - 1 - kL;
+    qbase[0] = 16 * kL;
+    qbase[QB - 1] = 16 * kH;
+    qon[0] = kL < kH;
+    qon[QB - 1] = kL <= kH;
+    i0 = 0;
+    const int kH0 = n16 - 1 - 4 * qblk;  // the workgroup's widest block
+    nkt = imin(N - 1, 16 * kH0 + 15) / 64 + 1;
+  } else {
+    i0 = qblk * kBM;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      qbase[qb] = i0 + kWQ * wave + 16 * qb;
+      qon[qb] = true;
+    }
+    const int ilast_b = imin(N - 1, i0 + kBM - 1);
+    nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
+  }
   const float sl2 = a.scale_log2;
   const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
   const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
   const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
   const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
 
-  // queries of this lane: iw + 16 qb + c16 (rows past N load as zero)
+  // queries of this lane: qbase[qb] + c16 (rows past N load as zero)
   bf16x8 qf[QB][2];
   float rlo[QB], rhi[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int i = iw + 16 * qb + c16;
+    const int i = qbase[qb] + c16;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       qf[qb][c] = __builtin_bit_cast(bf16x8, bload16(rq, static_cast<uint32_t>(i * 128 + 64 * c + 16 * g)));
-    const bool ok = i < N;
+    const bool ok = i < N && qon[qb];
     rlo[qb] = ok ? a.rowlo[tok + i] : 0.f;
     rhi[qb] = ok ? a.rowhi[tok + i] : 0.f;
   }
-  GroupInfo giq = {0, 0, 0, 0};
-  if (F & F_ZQ) giq = a.gq[iw / kGroup];
-  const int gq0 = (iw / kGroup) * kGroup;
+  // projection group of each block (a 16-query block lies in one group;
+  // without PAIR all of the wave's blocks share one)
+  GroupInfo giq[QB];
+  int gq0[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qg = qbase[PAIR ? qb : 0] / kGroup;
+    gq0[qb] = qg * kGroup;
+    giq[qb] = GroupInfo{0, 0, 0, 0};
+    if ((F & F_ZQ) && qon[qb]) giq[qb] = a.gq[qg];
+  }
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
     rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,
@@ -121,16 +159,21 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
 
-  // key tiles of the workgroup and of this wave
-  const int ilast_b = imin(N - 1, i0 + kBM - 1);
-  const int nkt = CAUSAL ? (ilast_b / 64 + 1) : (N + 63) / 64;
-  const int nkt_w = CAUSAL ? imin(nkt, (iw + kWQ - 1) / 64 + 1) : nkt;
-  // region bounds from the wave's extreme offsets: tiles [0, n_hi) have
-  // delta >= D for every pair, tiles [t_lo, nkt_w) have delta <= -D
-  int n_hi = (iw - D - 63 >= 0) ? (iw - D - 63) / 64 + 1 : 0;
-  n_hi = imin(n_hi, nkt_w);
-  int t_lo = CAUSAL ? nkt_w : (iw + kWQ - 1 + D + 63) / 64;
-  t_lo = imax(n_hi, imin(t_lo, nkt_w));
+  // key tiles of each block: [0, nkq) visible; region bounds from the
+  // block's extreme offsets: tiles [0, n_hi) have delta >= D for every pair,
+  // tiles [t_lo, nkq) have delta <= -D (without PAIR every block uses the
+  // wave's range)
+  int nkq[QB], n_hi[QB], t_lo[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qa = qbase[PAIR ? qb : 0], qz = qbase[PAIR ? qb : QB - 1] + 15;
+    nkq[qb] = !qon[qb] ? 0 : (CAUSAL ? imin(nkt, imin(N - 1, qz) / 64 + 1) : nkt);
+    const int nh = (qa - D - 63 >= 0) ? (qa - D - 63) / 64 + 1 : 0;
+    n_hi[qb] = imin(nh, nkq[qb]);
+    const int tl = CAUSAL ? nkq[qb] : (qz + D + 63) / 64;
+    t_lo[qb] = imax(n_hi[qb], imin(tl, nkq[qb]));
+  }
+  const int nkt_w = nkq[QB - 1];  // the last block reaches the most tiles
 
   float mu[QB], l[QB];
   floatx4 o[QB][4];
@@ -199,17 +242,36 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
       const bf16* Vs = sv[buf];
-      // region of the tile for this wave (uniform); on saturated tiles the
-      // key's boundary entry is the initial value of the S accumulator
-      const bool sat = kt < n_hi || kt >= t_lo;
-      const int side = kt < n_hi ? 1 : 0;  // 1: delta >= D (row 2D), 0: delta <= -D
+      // per block (uniform): does the tile reach it, and its region (1:
+      // delta >= D, row 2D; 0: delta <= -D); on saturated tiles the key's
+      // boundary entry is the initial value of the S accumulator.  A block
+      // the tile does not reach is block 0 (the last block is the widest).
+      bool act[QB], sat[QB];
+      int side[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        act[qb] = PAIR ? kt < nkq[qb] : true;
+        sat[qb] = kt < n_hi[qb] || kt >= t_lo[qb];
+        side[qb] = kt < n_hi[qb] ? 1 : 0;
+      }
       floatx4 s[QB][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (KC && sat) kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side : 2][16 * kb + 4 * g]);
+        if (!PAIR) {
+          floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (KC && sat[0])
+            kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[0] : 2][16 * kb + 4 * g]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = kx;
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = kx;
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (KC && sat[qb])
+              kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
+            s[qb][kb] = kx;
+          }
+        }
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -217,80 +279,104 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kKP + 32 * c + 8 * g);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
+          for (int qb = 0; qb < QB; ++qb) {
+            if (qb == 0 && !act[0]) continue;
             s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+          }
         }
       }
 
       // ---- relation terms: s becomes S plus the per-pair terms (score
       // units); off[qb] is the row's constant term (scaled) on saturated tiles
       float off[QB];
-      if (sat) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) off[qb] = (side ? rhi[qb] : rlo[qb]) * sl2;
-      } else {
+      auto band_terms = [&](int qb) {
         // band tile: per-pair terms; pairs with |delta| >= D take the
         // boundary entries
+        const int i = qbase[qb] + c16;
+        const bool iok = i < N;
+        const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int j1 = j0 + 16 * kb + 4 * g;
+          float zq[4] = {0.f, 0.f, 0.f, 0.f};
+          if (F & F_ZQ) {
+            const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+            const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            const halfx4 hv = __builtin_bit_cast(halfx4, w);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);  // descending
+          }
+          floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
+          if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
+          if (KC3) {
+            klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
+            khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
+          }
+          halfx4 zk4 = halfx4{0, 0, 0, 0};
+          if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
+            zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
+                                                     16 * kb + 4 * g, qbase[qb] - i0, c16));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int j = j1 + t;
+            const int dl = i - j;
+            // boundary pairs: the row's entry plus the key's
+            const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
+            float band = km[t] + zq[t];
+            if (F & F_ZK) band += static_cast<float>(zk4[t]);
+            if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+            s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+          }
+        }
+      };
+      auto mask_block = [&](int qb) {
+        const int i = qbase[qb] + c16;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int j = j0 + 16 * kb + 4 * g + t;
+            if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = -INFINITY;
+          }
+      };
+      if (!PAIR) {
+        // the wave's blocks share one region and one edge test
+        if (sat[0]) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) off[qb] = (side[0] ? rhi[qb] : rlo[qb]) * sl2;
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            off[qb] = 0.f;
+            band_terms(qb);
+          }
+        }
+        if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > qbase[0])) {
+          // (the empty asm keeps this a branch taken by the edge tiles only)
+          asm volatile("");
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mask_block(qb);
+        }
+      } else {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           off[qb] = 0.f;
-          const int i = iw + 16 * qb + c16;
-          const bool iok = i < N;
-          const int zrow = giq.base + (i - gq0) * giq.pitch;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const int j1 = j0 + 16 * kb + 4 * g;
-            float zq[4] = {0.f, 0.f, 0.f, 0.f};
-            if (F & F_ZQ) {
-              const int c0 = clamp_run((i - (j1 + 3) + D) - giq.slo + giq.pad, giq.pitch);
-              const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
-              const halfx4 hv = __builtin_bit_cast(halfx4, w);
-#pragma unroll
-              for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);  // descending
-            }
-            floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
-            if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
-            if (KC3) {
-              klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
-              khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
-            }
-            halfx4 zk4 = halfx4{0, 0, 0, 0};
-            if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
-              zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
-                                                       16 * kb + 4 * g, kWQ * wave + 16 * qb, c16));
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int j = j1 + t;
-              const int dl = i - j;
-              // boundary pairs: the row's entry plus the key's
-              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
-              float band = km[t] + zq[t];
-              if (F & F_ZK) band += static_cast<float>(zk4[t]);
-              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
-            }
+          if (!act[qb]) continue;
+          if (sat[qb])
+            off[qb] = (side[qb] ? rhi[qb] : rlo[qb]) * sl2;
+          else
+            band_terms(qb);
+          if ((j0 + 64 > N) || (j0 + 63 > qbase[qb])) {
+            asm volatile("");
+            mask_block(qb);
           }
-        }
-      }
-      if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > iw)) {
-        // (the empty asm keeps this a branch taken by the edge tiles only)
-        asm volatile("");
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int i = iw + 16 * qb + c16;
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int j = j0 + 16 * kb + 4 * g + t;
-              if (j >= N || (CAUSAL && j > i)) s[qb][kb][t] = -INFINITY;
-            }
         }
       }
 
       // ---- online softmax (base 2, lazy rescale)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        if (!act[qb]) continue;
         float mx = s[qb][0][0];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -350,6 +436,7 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
           }
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
+            if (qb == 0 && !act[0]) continue;
             o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[qb][db], 0, 0, 0);
             if (SPLIT)
               o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], o[qb][db], 0, 0, 0);
@@ -357,13 +444,16 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
         }
         if (!SPLIT) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
+          for (int qb = 0; qb < QB; ++qb) {
+            if (qb == 0 && !act[0]) continue;
             ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[qb], ls[qb], 0, 0, 0);
+          }
         }
       }
       if (!SPLIT) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb][0];
+        for (int qb = 0; qb < QB; ++qb)
+          if (act[qb]) l[qb] += ls[qb][0];
       }
     }
 
@@ -376,8 +466,8 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float ls = l[qb];  // the full row sum in every lane of the column
-    const int i = iw + 16 * qb + c16;
-    if (i >= N) continue;
+    const int i = qbase[qb] + c16;
+    if (i >= N || !qon[qb]) continue;
     const float inv = 1.f / ls;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -391,7 +481,10 @@ __global__ __launch_bounds__(256, (F & F_ZK) ? 2 : 3) void attn_fwd_fast(AttnArg
 
 template <int F>
 hipError_t launch_fast(const AttnArgs& a, int B, hipStream_t s) {
-  const int nqb = (a.N + kBM - 1) / kBM;
+  constexpr bool PAIR = (F & F_CAUSAL) && !(F & F_ZK);
+  // PAIR: workgroup m owns 16-query blocks 4m .. 4m+3 and their mirrors
+  const int n16 = (a.N + 15) / 16;
+  const int nqb = PAIR ? ((n16 + 1) / 2 + 3) / 4 : (a.N + kBM - 1) / kBM;
   const int total = nqb * B * a.H;
   const int xcd_map = (F & F_CAUSAL) ? 0 : 1;
   hipLaunchKernelGGL((attn_fwd_fast<F>), dim3(total), dim3(256), 0, s, a, nqb, total, xcd_map);

@@ -24,7 +24,7 @@ constexpr int kTP = 72;  // LDS pitch of a table tile (bf16), 144-byte rows
 __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   __shared__ __attribute__((aligned(16))) bf16 st[2][64 * kTP];
   __shared__ float sb[2][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.x;
   const int rb = nrb - 1 - static_cast<int>(blockIdx.y);
   const int h = bh % p.H;

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
   __shared__ __attribute__((aligned(16))) float zf[64 * kSP];
   __shared__ int so[64];
   __shared__ __attribute__((aligned(16))) bf16 at[64 * kRP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
   const int h = bh % f.H;
   const int64_t tok = static_cast<int64_t>(bh) * f.N;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];   // [token][d]
   __shared__ float bsh[2][64];
   __shared__ float p2red[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int D = p.D;
   // s tiles from the one holding offset 0 (s = D) outwards: those reach the
   // most tokens, so the longest blocks start first
