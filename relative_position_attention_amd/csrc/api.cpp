@@ -485,7 +485,8 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
-  const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0);
+  const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0) |
+                     (p.dzq_f16 ? F_DZ16 : 0);
   if (dt == 0)
     RP_HIP(launch_attn_bwd_q(dt, qflags, a, p.B, s));
   else
@@ -510,6 +511,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.causal = p.causal;
     f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
     f.dz_f32 = p.dzq_f32;
+    f.dz_f16 = p.dzq_f16;
     if (dt == 0)
       RP_HIP(launch_finalize(dt, f, p.BH, s));
     else
@@ -533,6 +535,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.key_side = 0;
     pa.causal = p.causal;
     pa.dz_f32 = p.dzq_f32;
+    pa.dz_f16 = p.dzq_f16;
     if (dt == 0)
       RP_HIP(launch_partials(dt, pa, s));
     else
@@ -631,6 +634,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.key_side = 1;
     pa.causal = p.causal;
     pa.dz_f32 = 0;
+    pa.dz_f16 = 0;
     if (dt == 0)
       RP_HIP(launch_partials(dt, pa, s));
     else

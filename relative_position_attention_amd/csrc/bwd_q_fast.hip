@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   constexpr bool DZ = (F & F_DZQ) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
-  using GT = typename DzType<bf16, (F & F_DZ32) != 0>::type;
+  using GT = std::conditional_t<(F & F_DZ16) != 0, _Float16,
+                                typename DzType<bf16, (F & F_DZ32) != 0>::type>;
   // key projections of a band tile are staged into LDS once per workgroup
   constexpr bool STZK = (F & F_ZK) != 0;
   // causal masks: pair each 16-query block with its mirror (below)
@@ -471,11 +472,12 @@ hipError_t launch_qf(const AttnArgs& a, int B, hipStream_t s) {
   X(F_ZQ | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_DZQ | F_DZ32) X(F_ZQ | F_U | F_DZQ)         \
   X(F_ZQ | F_U | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_U | F_DZQ) X(F_ZQ | F_ZK | F_U | F_DZQ | F_DZ32) \
   X(F_BT | F_DZQ | F_DZ32) X(F_BT | F_U | F_DZQ | F_DZ32) X(F_ZK | F_BT | F_DZQ | F_DZ32)  \
-  X(F_ZK | F_BT | F_U | F_DZQ | F_DZ32)
+  X(F_ZK | F_BT | F_U | F_DZQ | F_DZ32) X(F_ZQ | F_DZQ | F_DZ16) X(F_ZQ | F_U | F_DZQ | F_DZ16) \
+  X(F_ZQ | F_ZK | F_DZQ | F_DZ16) X(F_ZQ | F_ZK | F_U | F_DZQ | F_DZ16)
 
 template <int SPL>
 hipError_t dispatch_qf(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  const int f = flags & (F_ZQ | F_ZK | F_BT | F_U | F_CAUSAL | F_DZQ | F_DZ32);
+  const int f = flags & (F_ZQ | F_ZK | F_BT | F_U | F_CAUSAL | F_DZQ | F_DZ32 | F_DZ16);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \

@@ -127,6 +127,12 @@ __device__ __forceinline__ void store4(bf16* p, const float* in) {
   for (int t = 0; t < 4; ++t) v[t] = static_cast<bf16>(in[t]);
   *reinterpret_cast<bf16x4*>(p) = v;
 }
+__device__ __forceinline__ void store4(_Float16* p, const float* in) {
+  halfx4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = static_cast<_Float16>(in[t]);
+  *reinterpret_cast<halfx4*>(p) = v;
+}
 __device__ __forceinline__ void store4(float* p, const float* in) {
   floatx4 v;
 #pragma unroll

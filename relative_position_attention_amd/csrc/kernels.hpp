@@ -23,6 +23,7 @@ enum : int {
   F_U = 64,      // backward: key column sums of G (Transformer-XL u term)
   F_SPLIT = 128,  // bf16: P and G enter their MFMA products as bf16 hi + lo
   F_DZ32 = 256,   // backward: query-side offset gradients stored in fp32
+  F_DZ16 = 512,   // backward: query-side offset gradients stored in fp16
 };
 
 struct AttnArgs {
@@ -173,6 +174,7 @@ struct FinalizeArgs {
   void* out;            // out dtype
   int N, H, D, S, key_side, causal, out_f32;
   int dz_f32;  // entries are fp32
+  int dz_f16;  // entries are fp16
 };
 hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s);
 // bf16: aligned 16-byte staging of the offset gradients (reduce_fast.hip)
@@ -191,6 +193,7 @@ struct PartialArgs {
   float* p2;      // [H, nchunk, S] or null
   int B, N, H, D, S, nchunk, key_side, causal;
   int dz_f32;     // entries are fp32 (scalar bias without a query table)
+  int dz_f16;     // entries are fp16 (the Transformer-XL v term)
 };
 hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s);
 hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s);

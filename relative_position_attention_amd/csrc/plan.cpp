@@ -295,7 +295,13 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.g_size = p.t_size;  // offset gradients in the input precision
   // ... except where their plain sums are needed (a bias, or the v term):
   // fp32, since those sums cancel
-  p.dzq_f32 = p.bias || p.v;
+  // Precision of the query offset gradients: their per-offset sums over all
+  // queries feed db and dv, and every row of dS sums to zero, so these sums
+  // cancel.  A scalar bias (T5) keeps fp32 entries; the v term alone (TXL)
+  // needs 11 mantissa bits (fp16) rather than bf16's 8.
+  const bool f32in = p.dtype == RELPOS_DTYPE_F32;
+  p.dzq_f32 = p.bias || (p.v && f32in);
+  p.dzq_f16 = p.v && !p.bias && !f32in;
   p.split = desc->split_operands != 0 && p.dtype == RELPOS_DTYPE_BF16;
   bool any_table = p.aq || p.ak || p.bias;
   if (any_table && p.R < 1) {
@@ -475,7 +481,7 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   int64_t dz_elems = 0;
   if (p.need_qside) dz_elems = std::max(dz_elems, p.zq.bh_elems);
   if (p.ak) dz_elems = std::max(dz_elems, p.zk.bh_elems);
-  const size_t dz_entry = p.dzq_f32 ? 4 : p.g_size;
+  const size_t dz_entry = p.dzq_f32 ? 4 : (p.dzq_f16 ? 2 : p.g_size);
   p.ws_dz = off;
   off = align256(off + static_cast<size_t>(p.BH) * dz_elems * dz_entry);
   p.ws_bndq = off;

@@ -43,7 +43,8 @@ struct Plan {
   SideLayout zq, zk;  // projection / offset-gradient layouts (query side, key side)
   bool need_qside = false;  // query-side offset gradients exist (AQ, bias or v)
   size_t t_size = 2, z_size = 2, g_size = 2;
-  bool dzq_f32 = false;    // query-side offset gradients in fp32 (bias without A^Q)
+  bool dzq_f32 = false;    // query-side offset gradients in fp32 (a scalar bias)
+  bool dzq_f16 = false;    // query-side offset gradients in fp16 (v without a bias)
   bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
 

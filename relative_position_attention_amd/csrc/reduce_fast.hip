@@ -83,6 +83,11 @@ struct DzTile {
       float f[VEC];
       if constexpr (sizeof(GT) == 4) {
         __builtin_memcpy(f, &w[u], 16);
+      } else if constexpr (std::is_same_v<GT, _Float16>) {
+        _Float16 hv[8];
+        __builtin_memcpy(hv, &w[u], 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = static_cast<float>(hv[e]);
       } else {
         const uint32_t wd[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
@@ -437,6 +442,8 @@ hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s) {
   dim3 grid(f.causal ? (nrb + 1) / 2 : nrb, BH);
   if (f.dz_f32)
     hipLaunchKernelGGL((finalize_fast<float>), grid, dim3(256), 0, s, f);
+  else if (f.dz_f16)
+    hipLaunchKernelGGL((finalize_fast<_Float16>), grid, dim3(256), 0, s, f);
   else
     hipLaunchKernelGGL((finalize_fast<bf16>), grid, dim3(256), 0, s, f);
   return hipGetLastError();
@@ -446,6 +453,8 @@ hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s) {
   dim3 grid(nblk(p.S, 64), p.H, p.nchunk);
   if (p.dz_f32)
     hipLaunchKernelGGL((partials_fast<float>), grid, dim3(256), 0, s, p);
+  else if (p.dz_f16)
+    hipLaunchKernelGGL((partials_fast<_Float16>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((partials_fast<bf16>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
