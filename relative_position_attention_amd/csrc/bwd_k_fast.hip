@@ -283,6 +283,14 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         }
       }
 
+      // pure: a band tile without any pair |delta| >= D (every tile of an
+      // identity map), whose selects are skipped
+      bool pure[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int ja = jbase[PAIR ? kb : 0], jz = jbase[PAIR ? kb : 1] + 15;
+        pure[kb] = i0 - jz > -D && i0 + kT - 1 - ja < D;
+      }
       bool need_mask[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -337,14 +345,25 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
             if (STZQ)  // Z^Q[i1 + t][i1 + t - j + D], t = 0..3
               zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq), kZP,
                                                        16 * qb + 4 * g, jloc[kb], c16));
+            if (pure[kb]) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int i = i1 + t;
-              const int dl = i - j;
-              float band = kmid[kb] + zk[t];
-              if (F & F_ZQ) band += static_cast<float>(zq4[t]);
-              if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-              rel[t] = dl >= D ? (qrh[t] + khi[kb]) : (dl <= -D ? (qrl[t] + klo[kb]) : band);
+              for (int t = 0; t < 4; ++t) {
+                float band = kmid[kb] + zk[t];
+                if (F & F_ZQ) band += static_cast<float>(zq4[t]);
+                if (F & F_BT)
+                  band += bloadf(rbt, static_cast<uint32_t>(iclamp(i1 + t - j + D, 0, 2 * D) * 4));
+                rel[t] = band;
+              }
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const int i = i1 + t;
+                const int dl = i - j;
+                float band = kmid[kb] + zk[t];
+                if (F & F_ZQ) band += static_cast<float>(zq4[t]);
+                if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+                rel[t] = dl >= D ? (qrh[t] + khi[kb]) : (dl <= -D ? (qrl[t] + klo[kb]) : band);
+              }
             }
           }
 #pragma unroll
@@ -401,21 +420,30 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
               } else {
                 float run[4];
                 bool any = false;
+                if (pure[kb]) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const int i = i1 + t;
-                  const int dl = i - j;
-                  const float gg = dp[qb][kb][t];
-                  float bandv = 0.f;
-                  if (dl >= D)
-                    bhi[kb] += gg;
-                  else if (dl <= -D)
-                    blo[kb] += gg;
-                  else {
-                    bandv = tau * gg;
+                  for (int t = 0; t < 4; ++t) {
+                    const int i = i1 + t;
+                    run[t] = tau * dp[qb][kb][t];  // ascending columns
                     any = any || (i < N && j < N && (!CAUSAL || j <= i));
                   }
-                  run[t] = bandv;  // ascending columns
+                } else {
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) {
+                    const int i = i1 + t;
+                    const int dl = i - j;
+                    const float gg = dp[qb][kb][t];
+                    float bandv = 0.f;
+                    if (dl >= D)
+                      bhi[kb] += gg;
+                    else if (dl <= -D)
+                      blo[kb] += gg;
+                    else {
+                      bandv = tau * gg;
+                      any = any || (i < N && j < N && (!CAUSAL || j <= i));
+                    }
+                    run[t] = bandv;  // ascending columns
+                  }
                 }
                 if (any) {
                   bf16* row = reinterpret_cast<bf16*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh +

@@ -266,16 +266,17 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       }
 
       // relation terms (same values as the forward); off = the row's
-      // constant on saturated tiles
-      float off[2];
+      // constant on saturated tiles.  pure: a band tile without any pair
+      // |delta| >= D (every tile of an identity map), whose selects are
+      // skipped
+      bool pure[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        off[qb] = 0.f;
-        if (!act[qb]) continue;
-        if (sat[qb]) {
-          off[qb] = side[qb] ? rhi[qb] : rlo[qb];
-          continue;
-        }
+        const int qa = qbase[PAIR ? qb : 0], qz = qbase[PAIR ? qb : 1] + 15;
+        pure[qb] = qa - (j0 + 63) > -D && qz - j0 < D;
+      }
+      float off[2];
+      auto band_q = [&](int qb, auto PURE) {
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           }
           floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
           if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
-          if (KC3) {
+          if (KC3 && !PURE) {
             klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
             khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
           }
@@ -304,15 +305,30 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           for (int t = 0; t < 4; ++t) {
             const int j = j1 + t;
             const int dl = i - j;
-            const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
             float band = km[t] + zq[t];
             if (F & F_ZK) band += static_cast<float>(zk4[t]);
             if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-            s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            if constexpr (PURE) {
+              s[qb][kb][t] += band;
+            } else {
+              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
+              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            }
           }
           // keep each 4-run's loads next to their use (register pressure)
           __builtin_amdgcn_sched_barrier(0);
         }
+      };
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        off[qb] = 0.f;
+        if (!act[qb]) continue;
+        if (sat[qb])
+          off[qb] = side[qb] ? rhi[qb] : rlo[qb];
+        else if (pure[qb])
+          band_q(qb, std::true_type{});
+        else
+          band_q(qb, std::false_type{});
       }
 
       // P, then G' = P (dP - D) in place of s; tau is applied to the sums
@@ -370,29 +386,35 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           }
           const int i = qbase[qb] + c16;
           GT* rowp = dzslice + giq[qb].base + static_cast<int64_t>(i - gq0[qb]) * giq[qb].pitch;
+          auto dz_band = [&](auto PURE) {
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const int j1 = j0 + 16 * kb + 4 * g;
-            float run[4];
-            bool any = false;
+            for (int kb = 0; kb < 4; ++kb) {
+              const int j1 = j0 + 16 * kb + 4 * g;
+              float run[4];
+              bool any = false;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int j = j1 + t;
-              const int dl = i - j;
-              const float gg = s[qb][kb][t];
-              float bandv = 0.f;  // tau G' for the band entry
-              if (dl >= D)
-                bhi[qb] += gg;
-              else if (dl <= -D)
-                blo[qb] += gg;
-              else {
-                bandv = tau * gg;
-                any = any || (i < N && j < N && (!CAUSAL || j <= i));
+              for (int t = 0; t < 4; ++t) {
+                const int j = j1 + t;
+                const int dl = i - j;
+                const float gg = s[qb][kb][t];
+                float bandv = 0.f;  // tau G' for the band entry
+                if (!PURE && dl >= D)
+                  bhi[qb] += gg;
+                else if (!PURE && dl <= -D)
+                  blo[qb] += gg;
+                else {
+                  bandv = tau * gg;
+                  any = any || (i < N && j < N && (!CAUSAL || j <= i));
+                }
+                run[3 - t] = bandv;  // descending columns
               }
-              run[3 - t] = bandv;  // descending columns
+              if (any) store4(rowp + ((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad), run);
             }
-            if (any) store4(rowp + ((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad), run);
-          }
+          };
+          if (pure[qb])
+            dz_band(std::true_type{});
+          else
+            dz_band(std::false_type{});
         }
       }
 

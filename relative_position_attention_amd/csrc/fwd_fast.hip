@@ -289,9 +289,10 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
       // ---- relation terms: s becomes S plus the per-pair terms (score
       // units); off[qb] is the row's constant term (scaled) on saturated tiles
       float off[QB];
-      auto band_terms = [&](int qb) {
-        // band tile: per-pair terms; pairs with |delta| >= D take the
-        // boundary entries
+      // band tile: per-pair terms; pairs with |delta| >= D take the boundary
+      // entries (PURE: the tile holds no such pair, as every tile of an
+      // identity map does, and the selects are skipped)
+      auto band_terms = [&](int qb, auto PURE) {
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
           }
           floatx4 km = floatx4{0.f, 0.f, 0.f, 0.f}, klo4 = km, khi4 = km;
           if (KC) km = *reinterpret_cast<const floatx4*>(&skc[buf][2][16 * kb + 4 * g]);
-          if (KC3) {
+          if (KC3 && !PURE) {
             klo4 = *reinterpret_cast<const floatx4*>(&skc[buf][0][16 * kb + 4 * g]);
             khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
           }
@@ -320,12 +321,16 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
           for (int t = 0; t < 4; ++t) {
             const int j = j1 + t;
             const int dl = i - j;
-            // boundary pairs: the row's entry plus the key's
-            const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
             float band = km[t] + zq[t];
             if (F & F_ZK) band += static_cast<float>(zk4[t]);
             if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-            s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            if constexpr (PURE) {
+              s[qb][kb][t] += band;
+            } else {
+              // boundary pairs: the row's entry plus the key's
+              const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
+              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+            }
           }
         }
       };
@@ -345,10 +350,14 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) off[qb] = (side[0] ? rhi[qb] : rlo[qb]) * sl2;
         } else {
+          const bool pure = qbase[0] - (j0 + 63) > -D && qbase[QB - 1] + 15 - j0 < D;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             off[qb] = 0.f;
-            band_terms(qb);
+            if (pure)
+              band_terms(qb, std::true_type{});
+            else
+              band_terms(qb, std::false_type{});
           }
         }
         if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > qbase[0])) {
@@ -364,8 +373,10 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
           if (!act[qb]) continue;
           if (sat[qb])
             off[qb] = (side[qb] ? rhi[qb] : rlo[qb]) * sl2;
+          else if (qbase[qb] - (j0 + 63) > -D && qbase[qb] + 15 - j0 < D)
+            band_terms(qb, std::true_type{});
           else
-            band_terms(qb);
+            band_terms(qb, std::false_type{});
           if ((j0 + 64 > N) || (j0 + 63 > qbase[qb])) {
             asm volatile("");
             mask_block(qb);
