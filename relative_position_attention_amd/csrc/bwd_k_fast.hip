@@ -41,10 +41,12 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   // causal masks: pair each 16-key block with its mirror (below)
   constexpr bool PAIR = CAUSAL && !(F & F_ZK) && !DZ;
   constexpr int kZP = 136;  // szq pitch (fp16)
-  __shared__ __attribute__((aligned(16))) _Float16 szq[STZQ ? kT * kZP : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 szq[2][STZQ ? kT * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sq[2][kT * kP];
   __shared__ __attribute__((aligned(16))) bf16 sd[2][kT * kP];
-  __shared__ __attribute__((aligned(16))) float sqs[2][4][kT];  // l2, D, rowlo, rowhi
+  // l2, D, rowlo, rowhi (rows 4..7: unread copies, written by threads 128..255
+  // so that the store needs no branch)
+  __shared__ __attribute__((aligned(16))) float sqs[2][8][kT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
@@ -164,30 +166,74 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
   const int kr = tid >> 3, kc8 = (tid & 7) * 8;
   // a query tile in registers on its way to LDS: Q and dO rows (t >> 3), chunk
-  // t & 7, and for t < 32 the query's L (log2 units), D and boundary entries
+  // t & 7, and one per-query value: thread t < 128 holds value (t >> 5) (L, D
+  // and the two boundary entries) of query t & 31 (threads past 128 repeat
+  // those loads).  Every load is issued unconditionally, rows past N reading
+  // zero or a clamped index, so that each wave issues the same vector loads on
+  // every path and the compiler's wait counts stay exact.
+  const int sx = (tid >> 5) & 3, sqi = tid & 31;
+  const float* const sbase = sx == 0 ? a.lse : (sx == 1 ? a.dvec : (sx == 2 ? a.rowlo : a.rowhi));
   struct TileRegs {
     uint4 q, d;
-    float s[4];
+    float st;
   };
   auto load_tile = [&](TileRegs& r, int i0) {
     const uint32_t off = static_cast<uint32_t>((i0 + kr) * 128 + kc8 * 2);
     r.q = bload16(rq, off);
     r.d = bload16(rdo, off);
-    if (tid < kT) {
-      const int i = i0 + tid;
-      const bool ok = i < N;
-      r.s[0] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
-      r.s[1] = ok ? a.dvec[tok + i] : 0.f;
-      r.s[2] = ok ? a.rowlo[tok + i] : 0.f;
-      r.s[3] = ok ? a.rowhi[tok + i] : 0.f;
-    }
+    r.st = sbase[tok + imin(i0 + sqi, N - 1)];
   };
-  auto store_tile = [&](const TileRegs& r, int buf) {
+  auto store_tile = [&](const TileRegs& r, int buf, int i0) {
     *reinterpret_cast<uint4*>(&sq[buf][kr * kP + kc8]) = r.q;
     *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = r.d;
-    if (tid < kT) {
+    // L enters log2 units; padding rows get L = inf (P = 0) and zeros
+    const bool ok = i0 + sqi < N;
+    const float v = sx == 0 ? (ok ? r.st * kLog2e : INFINITY) : (ok ? r.st : 0.f);
+    sqs[buf][tid >> 5][sqi] = v;
+  };
+
+  // Z^Q of a tile's queries for the workgroup's keys (band tiles), staged as
+  // szq[query][key column]: a query row holds 64 consecutive keys in
+  // descending order from a 16-byte boundary (the query-side pad), so each
+  // chunk is reversed.  Columns 0..63 are keys j0b.., 64..127 keys j0b + 64..
+  // (PAIR: keys jrB..).  The loads of tile t + 1 are issued during tile t
+  // (before that step's tile prefetch) and written at its end.
+  uint4 zr[2];
+  auto load_zq = [&](int t) {
+    const int i0 = t * kT;
+    const int jr0 = j0b, jr1 = PAIR ? jrB : j0b + 64;
+    const bool sat0 = (i0 - (jr0 + 63) >= D) || (i0 + kT - 1 - jr0 <= -D);
+    const bool sat1 = (i0 - (jr1 + 63) >= D) || (i0 + kT - 1 - jr1 <= -D);
+    const bool need = t < nqt && !(sat0 && sat1);
+    GroupInfo gq = {0, 0, 0, 0};
+    if (need) gq = sload_uniform16(a.gq + i0 / kGroup);
+    const int gq0s = (i0 / kGroup) * kGroup;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) sqs[buf][x][tid] = r.s[x];
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      const int r = idx >> 4, ch = idx & 15;
+      const int half = ch >> 3, chl = ch & 7;
+      const int jtop = (half ? jr1 : jr0) + 63;
+      const int i = i0 + r;
+      const int col = (i - jtop + D) - gq.slo + gq.pad + 8 * chl;
+      const int e = gq.base + (i - gq0s) * gq.pitch + col;
+      zr[u] = bload16(rzq, (need && i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
+    }
+  };
+  auto store_zq = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u;
+      const int r = idx >> 4, ch = idx & 15;
+      const int half = ch >> 3, chl = ch & 7;
+      // entries 8 chl .. 8 chl + 7 of the run are keys jtop - 8 chl - (0..7)
+      const uint4 w = zr[u];
+      uint4 rev;
+      rev.x = __builtin_amdgcn_perm(w.w, w.w, 0x01000302u);
+      rev.y = __builtin_amdgcn_perm(w.z, w.z, 0x01000302u);
+      rev.z = __builtin_amdgcn_perm(w.y, w.y, 0x01000302u);
+      rev.w = __builtin_amdgcn_perm(w.x, w.x, 0x01000302u);
+      *reinterpret_cast<uint4*>(szq[buf] + r * kZP + (64 * half + 56 - 8 * chl)) = rev;
     }
   };
 
@@ -195,13 +241,14 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   // is in flight in one register set and tile t + 2 is requested into the
   // other (the loads of a tile get two tiles' time to arrive).
   TileRegs ra, rb;
-  ra.s[0] = ra.s[1] = ra.s[2] = ra.s[3] = 0.f;
-  rb.s[0] = rb.s[1] = rb.s[2] = rb.s[3] = 0.f;
-  if (it0 < nqt) {
-    load_tile(ra, it0 * kT);
-    store_tile(ra, 0);
+  load_tile(ra, it0 * kT);
+  store_tile(ra, 0, it0 * kT);
+  if (STZQ) {
+    load_zq(it0);
+    store_zq(0);
   }
-  if (it0 + 1 < nqt) load_tile(rb, (it0 + 1) * kT);
+  wait_vm_all();
+  load_tile(rb, (it0 + 1) * kT);
   __syncthreads();
 
   // one tile step: rl held tile it (already in LDS) and now receives tile
@@ -209,40 +256,8 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   auto tile_step = [&](int it, TileRegs& rl, TileRegs& rs) {
     const int buf = (it - it0) & 1;
     const int i0 = it * kT;
-    if (it + 2 < nqt) load_tile(rl, i0 + 2 * kT);
-    if (STZQ) {
-      // band for some wave of the workgroup: stage Z^Q of the tile's queries
-      // for the workgroup's keys, as szq[query][key column]; a query row holds
-      // 64 consecutive keys in descending order from a 16-byte boundary (the
-      // query-side pad), so each chunk is reversed.  Columns 0..63 are keys
-      // j0b.., 64..127 keys j0b + 64.. (PAIR: keys jrB..).
-      const int jr0 = j0b, jr1 = PAIR ? jrB : j0b + 64;
-      const bool sat0 = (i0 - (jr0 + 63) >= D) || (i0 + kT - 1 - jr0 <= -D);
-      const bool sat1 = (i0 - (jr1 + 63) >= D) || (i0 + kT - 1 - jr1 <= -D);
-      if (!(sat0 && sat1)) {
-        const GroupInfo gq = a.gq[i0 / kGroup];
-        const int gq0s = (i0 / kGroup) * kGroup;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int idx = tid + 256 * u;
-          const int r = idx >> 4, ch = idx & 15;
-          const int half = ch >> 3, chl = ch & 7;
-          const int jtop = (half ? jr1 : jr0) + 63;
-          const int i = i0 + r;
-          const int col = (i - jtop + D) - gq.slo + gq.pad + 8 * chl;
-          const int e = gq.base + (i - gq0s) * gq.pitch + col;
-          const uint4 w = bload16(rzq, (i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
-          // entries 8 chl .. 8 chl + 7 of the run are keys jtop - 8 chl - (0..7)
-          uint4 rev;
-          rev.x = __builtin_amdgcn_perm(w.w, w.w, 0x01000302u);
-          rev.y = __builtin_amdgcn_perm(w.z, w.z, 0x01000302u);
-          rev.z = __builtin_amdgcn_perm(w.y, w.y, 0x01000302u);
-          rev.w = __builtin_amdgcn_perm(w.x, w.x, 0x01000302u);
-          *reinterpret_cast<uint4*>(szq + r * kZP + (64 * half + 56 - 8 * chl)) = rev;
-        }
-        __syncthreads();
-      }
-    }
+    if (STZQ) load_zq(it + 1);
+    load_tile(rl, i0 + 2 * kT);
 
     if (it >= itw) {
       const bf16* Qs = sq[buf];
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
             }
             halfx4 zq4 = halfx4{0, 0, 0, 0};
             if (STZQ)  // Z^Q[i1 + t][i1 + t - j + D], t = 0..3
-              zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq), kZP,
+              zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq[buf]), kZP,
                                                        16 * qb + 4 * g, jloc[kb], c16));
             if (pure[kb]) {
 #pragma unroll
@@ -501,12 +516,19 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       }
     }
 
-    if (it + 1 < nqt) store_tile(rs, buf ^ 1);
+    // (stored also after the last tile, into the buffer no one reads again:
+    // with no branch around them the compiler's wait counts stay exact)
+    store_tile(rs, buf ^ 1, i0 + kT);
+    if (STZQ) store_zq(buf ^ 1);
     __syncthreads();
   };
-  for (int it = it0; it < nqt; it += 2) {
+  // two steps per iteration so the register sets swap roles without copies;
+  // the loop is left from either step, so the back edge carries exact counts
+  for (int it = it0;;) {
     tile_step(it, ra, rb);
-    if (it + 1 < nqt) tile_step(it + 1, rb, ra);
+    if (++it >= nqt) break;
+    tile_step(it, rb, ra);
+    if (++it >= nqt) break;
   }
 
 #pragma unroll

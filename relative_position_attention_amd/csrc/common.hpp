@@ -202,6 +202,31 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
+// Wait for every outstanding vector memory load of the wave (s_waitcnt
+// vmcnt(0), the other counters left free).  Used once after the loads that
+// precede a tile loop on a conditional path: without it the compiler cannot
+// prove those loads done at the loop header and waits for vmcnt(0) inside
+// the loop, where the count then covers the loop's own prefetches.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scalar-memory load of a 16-byte record at a wave-uniform address, waited for
+// in place.  Scalar loads are counted apart from vector loads, so a loop that
+// needs such a record every tile does not wait for its own vector prefetches.
+template <typename T>
+__device__ __forceinline__ T sload_uniform16(const T* p) {
+  static_assert(sizeof(T) == 16, "16-byte records only");
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  // (readfirstlane returns int: each half goes through uint32 before the
+  // widening, so the low half is zero-extended, not sign-extended)
+  const unsigned long long u = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(u & 0xffffffffu)));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  const unsigned long long q = (static_cast<unsigned long long>(hi) << 32) | static_cast<unsigned long long>(lo);
+  v4i v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
+  return __builtin_bit_cast(T, v);
+}
+
 // ---- buffer resources: 32-bit offsets, loads past `bytes` return zero (the
 // hardware range check replaces per-lane bounds branches)
 typedef __amdgpu_buffer_rsrc_t Rsrc;
