@@ -60,10 +60,17 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
   // causal masks: pair each 16-query block with its mirror (below)
   constexpr bool PAIR = CAUSAL && !STZK;
   constexpr int kZP = 136;  // szk pitch (fp16)
+  // Z^Q runs of band tiles under causal masks (every tile of an identity map
+  // is a band tile): issued for all blocks at the top of the step, before the
+  // next tile's prefetch, so that waiting for them leaves the prefetch in
+  // flight.  Elsewhere band tiles are few and the runs are loaded where used.
+  constexpr bool HOIST = (F & F_ZQ) && CAUSAL;
   __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
   __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kKP];
-  __shared__ __attribute__((aligned(16))) float skc[2][3][64];
+  // per key: boundary entries lo, hi and the band constant (row 3: unread
+  // copies, written so that the store needs no branch)
+  __shared__ __attribute__((aligned(16))) float skc[2][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
@@ -185,59 +192,77 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
     for (int db = 0; db < 4; ++db) o[qb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // tile staging: K and V rows (t>>3) and 32 + (t>>3), chunk t&7
+  // tile staging: K and V rows (t>>3) and 32 + (t>>3), chunk t&7, and one
+  // per-key value per thread (value tid >> 6 of key tid & 63).  Every load is
+  // issued unconditionally (rows past N read zero, indexes are clamped), so
+  // each wave issues the same vector loads on every path and the compiler's
+  // wait counts stay exact.
   const int kr = tid >> 3, kc8 = (tid & 7) * 8;
   uint4 tk[2], tv[2];
-  float tkc[3] = {0.f, 0.f, 0.f};
+  float tkc = 0.f;
+  const int kcx = tid >> 6, kcj = tid & 63;
+  const float* const kbase = (KC3 && kcx == 0) ? a.keylo : ((KC3 && kcx == 1) ? a.keyhi : a.keymid);
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       tk[u] = bload16(rk, static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2));
       tv[u] = bload16(rv, static_cast<uint32_t>((j0 + kr + 32 * u) * 128 + kc8 * 2));
     }
-    if (KC && tid < 64) {
-      const int j = j0 + tid;
-      const bool ok = j < N;
-      tkc[2] = ok ? a.keymid[tok + j] : 0.f;
-      if (KC3) {
-        tkc[0] = ok ? a.keylo[tok + j] : 0.f;
-        tkc[1] = ok ? a.keyhi[tok + j] : 0.f;
-      }
-    }
+    if (KC) tkc = kbase[tok + imin(j0 + kcj, N - 1)];
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int j0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       *reinterpret_cast<uint4*>(&sk[buf][(kr + 32 * u) * kKP + kc8]) = tk[u];
       *reinterpret_cast<uint4*>(&sv[buf][(kr + 32 * u) * kKP + kc8]) = tv[u];
     }
-    if (KC && tid < 64) {
-      skc[buf][2][tid] = tkc[2];
-      if (KC3) {
-        skc[buf][0][tid] = tkc[0];
-        skc[buf][1][tid] = tkc[1];
-      }
-    }
+    if (KC) skc[buf][kcx][kcj] = j0 + kcj < N ? tkc : 0.f;
   };
 
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
+  wait_vm_all();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     const int j0 = kt * 64;
-    if (kt + 1 < nkt) load_tile(j0 + 64);
     if (STZK) {
       // band for some wave of the workgroup: stage Z^K of the tile's keys
+      // (before the next tile's prefetch is issued, so the staging's waits
+      // do not cover it; the group record comes through the scalar cache)
       const bool blk_sat = (i0 - (j0 + 63) >= D) || (i0 + kBM - 1 - j0 <= -D);
       if (!blk_sat && j0 < N) {
-        const GroupInfo gk = a.gk[j0 / kGroup];
+        const GroupInfo gk = sload_uniform16(a.gk + j0 / kGroup);
         stage_zk_rows(rzk, gk.base, gk.slo, gk.pad, gk.pitch, (j0 / kGroup) * kGroup, j0, i0, D,
                       szk, kZP);
         __syncthreads();
       }
     }
+    // Z^Q runs of this tile's band blocks, then the next tile's prefetch: in
+    // this order the wait for the runs leaves the prefetch in flight, and the
+    // runs of all blocks are in flight together.  Lane (c16, g) of block qb
+    // reads Z^Q[i][i - j1 - t + D], t = 0..3, i = qbase + c16,
+    // j1 = j0 + 16 kb + 4g (a run in descending column order).
+    uint2 zqr[QB][4];
+    if (HOIST) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool bandq = kt < nkt_w && (PAIR ? kt < nkq[qb] : true) &&
+                           !(kt < n_hi[qb] || kt >= t_lo[qb]);
+        const int i = qbase[qb] + c16;
+        const bool iok = bandq && i < N;
+        const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int j1 = j0 + 16 * kb + 4 * g;
+          const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+          zqr[qb][kb] = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+        }
+      }
+    }
+    if (HOIST) __builtin_amdgcn_sched_barrier(0);
+    load_tile(j0 + 64);
 
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
@@ -301,8 +326,13 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
           const int j1 = j0 + 16 * kb + 4 * g;
           float zq[4] = {0.f, 0.f, 0.f, 0.f};
           if (F & F_ZQ) {
-            const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
-            const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            uint2 w;
+            if (HOIST) {
+              w = zqr[qb][kb];
+            } else {
+              const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+              w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            }
             const halfx4 hv = __builtin_bit_cast(halfx4, w);
 #pragma unroll
             for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);  // descending
@@ -469,8 +499,9 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
     }
 
     // buffer buf ^ 1 was last read in iteration kt - 1, which every wave
-    // finished before the previous barrier
-    if (kt + 1 < nkt) store_tile(buf ^ 1);
+    // finished before the previous barrier (stored also after the last tile,
+    // into the buffer no one reads again)
+    store_tile(buf ^ 1, j0 + 64);
     __syncthreads();
   }
 
