@@ -38,7 +38,9 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   const Rsrc ra = make_rsrc(reinterpret_cast<const bf16*>(p.at) +
                                 static_cast<int64_t>(p.at_shared ? 0 : h) * p.S * 64,
                             static_cast<uint64_t>(p.S) * 128);
-  const float* btab = p.bt != nullptr ? p.bt + static_cast<int64_t>(h) * p.S : nullptr;
+  // (no bias table: a resource of size zero, whose loads all read zero)
+  const Rsrc rbt = make_rsrc(p.bt != nullptr ? p.bt + static_cast<int64_t>(h) * p.S : nullptr,
+                             p.bt != nullptr ? static_cast<uint64_t>(p.S) * 4 : 0);
 
   // A operand: rows r0 + 16 wave + c16 (rows past N read zero)
   const int rw = r0 + 16 * wave;
@@ -47,7 +49,12 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   for (int c = 0; c < 2; ++c)
     af[c] = __builtin_bit_cast(bf16x8, bload16(rx, static_cast<uint32_t>((rw + c16) * 128 + 64 * c + 16 * g)));
 
-  // table tile staging: row tid >> 2 of the tile, 16 elements at (tid & 3) * 16
+  // table tile staging: row tid >> 2 of the tile, 16 elements at (tid & 3) * 16,
+  // and the bias of column tid & 63 (threads past 64 repeat those loads).
+  // Every load and store below is issued unconditionally (clamped rows,
+  // out-of-range buffer offsets for entries past the window), so each wave
+  // issues the same memory instructions on every path: the wait for the next
+  // table tile then never covers the stores still in flight.
   const int ar = tid >> 2, ac = (tid & 3) * 16;
   uint4 ta[2];
   float tb = 0.f;
@@ -55,10 +62,8 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
     const int s = iclamp(c0 + ar - gi.pad + gi.slo, 0, D2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) ta[u] = bload16(ra, static_cast<uint32_t>(s * 128 + (ac + 8 * u) * 2));
-    if (tid < 64) {
-      const int sc = iclamp(c0 + tid - gi.pad + gi.slo, 0, D2);
-      tb = btab != nullptr ? btab[sc] : 0.f;
-    }
+    const int sc = iclamp(c0 + (tid & 63) - gi.pad + gi.slo, 0, D2);
+    tb = bloadf(rbt, static_cast<uint32_t>(sc) * 4);
   };
   auto store_tab = [&](int buf) {
 #pragma unroll
@@ -66,15 +71,17 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
     if (tid < 64) sb[buf][tid] = tb;
   };
 
-  _Float16* z = reinterpret_cast<_Float16*>(p.z) + static_cast<int64_t>(bh) * p.z_bh + gi.base;
+  const Rsrc rz = make_rsrc(reinterpret_cast<_Float16*>(p.z) + static_cast<int64_t>(bh) * p.z_bh,
+                            static_cast<uint64_t>(p.z_bh) * 2);
   const int nct = (gi.pitch + 63) / 64;
   load_tab(0);
   store_tab(0);
+  wait_vm_all();
   __syncthreads();
   for (int t = 0; t < nct; ++t) {
     const int buf = t & 1;
     const int c0 = t * 64;
-    if (t + 1 < nct) load_tab(c0 + 64);
+    load_tab(c0 + 64);
     floatx4 acc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
@@ -86,22 +93,24 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[c], bfr, acc[cb], 0, 0, 0);
       }
     }
-    // lane holds rows rw + 4g + e, column c0 + 16 cb + c16
+    // lane holds rows rw + 4g + e, column c0 + 16 cb + c16 (entries past the
+    // row's window or past N are dropped by the buffer range check)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int cl = 16 * cb + c16;
       const int col = c0 + cl;
       const float add = sb[buf][cl];
-      if (col < gi.pitch) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = rw + 4 * g + e;
-          if (i < p.N)
-            z[static_cast<int64_t>(i - grp * kGroup) * gi.pitch + col] = from_f<_Float16>(acc[cb][e] + add);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int i = rw + 4 * g + e;
+        const bool ok = col < gi.pitch && i < p.N;
+        const uint32_t off = ok ? static_cast<uint32_t>(gi.base + (i - grp * kGroup) * gi.pitch + col) * 2 : kOob;
+        const _Float16 v = from_f<_Float16>(acc[cb][e] + add);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rz, off, 0, 0);
       }
     }
-    if (t + 1 < nct) store_tab(buf ^ 1);
+    // (the tile after the last is staged too, into the buffer no one reads)
+    store_tab(buf ^ 1);
     __syncthreads();
   }
 }
