@@ -256,6 +256,24 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   auto tile_step = [&](int it, TileRegs& rl, TileRegs& rs) {
     const int buf = (it - it0) & 1;
     const int i0 = it * kT;
+    // Z^K runs of this band tile (key tables): issued first, so that waiting
+    // for them leaves the prefetches below in flight.  Lane (c16, g) of
+    // blocks (qb, kb) reads Z^K[j][i1 - j + D], i1 = i0 + 16 qb + 4g + t,
+    // t = 0..3, j = jbase[kb] + c16 (an ascending run).
+    uint2 zkr[2][2];
+    if (F & F_ZK) {
+      const bool bandk = it >= itw && !(it < n_lo[0] || it >= t_hi[0]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int i1 = i0 + 16 * qb + 4 * g;
+          const int j = jbase[kb] + c16;
+          const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
+          zkr[qb][kb] = bload8(rzk, (bandk && j < N)
+              ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + c0) * 2) : kOob);
+        }
+    }
     if (STZQ) load_zq(it + 1);
     load_tile(rl, i0 + 2 * kT);
 
@@ -349,10 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
           {
             float zk[4] = {0.f, 0.f, 0.f, 0.f};
             if (F & F_ZK) {
-              const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
-              const uint32_t offk = j < N
-                  ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + c0) * 2) : kOob;
-              const halfx4 hv = __builtin_bit_cast(halfx4, bload8(rzk, offk));
+              const halfx4 hv = __builtin_bit_cast(halfx4, zkr[qb][kb]);
 #pragma unroll
               for (int t = 0; t < 4; ++t) zk[t] = static_cast<float>(hv[t]);  // ascending
             }
@@ -414,6 +429,15 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int t = 0; t < 4; ++t) dp[qb][kb][t] = s[qb][kb][t] * (dp[qb][kb][t] - qdd[t]);
+      }
+
+      // with key offset gradients the next tiles go to the other LDS buffers
+      // (last read in the previous step, before its closing barrier) here,
+      // ahead of the offset-gradient stores, so the waits for their loads do
+      // not count those stores
+      if (DZ) {
+        store_tile(rs, buf ^ 1, i0 + kT);
+        if (STZQ) store_zq(buf ^ 1);
       }
 
       // key offset gradients and column sums
@@ -518,8 +542,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
     // (stored also after the last tile, into the buffer no one reads again:
     // with no branch around them the compiler's wait counts stay exact)
-    store_tile(rs, buf ^ 1, i0 + kT);
-    if (STZQ) store_zq(buf ^ 1);
+    if (!DZ || it < itw) {
+      store_tile(rs, buf ^ 1, i0 + kT);
+      if (STZQ) store_zq(buf ^ 1);
+    }
     __syncthreads();
   };
   // two steps per iteration so the register sets swap roles without copies;
