@@ -245,14 +245,45 @@ __global__ __launch_bounds__(256) void rowkey_kernel(RowKeyArgs a, int64_t rows)
 }
 
 // D_i = <dO_i, O_i> ([RPA] Table 9 "Preprocessing")
+// Eight lanes per row, eight consecutive elements each (one or two 16-byte
+// loads per operand, so a wave reads eight whole rows); the eight partial
+// sums meet in a fixed butterfly, so the result is the same on every call.
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float* v) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(wd[k] << 16);
+      v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+    }
+  }
+}
+
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void rowdot_kernel(const TO* o, const T* dout, float* dvec,
                                                      int64_t rows) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (row >= rows) return;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> 3;
+  const int part = static_cast<int>(gid & 7);
   float acc = 0.f;
-  for (int c = 0; c < 64; ++c) acc += to_f(o[row * 64 + c]) * to_f(dout[row * 64 + c]);
-  dvec[row] = acc;
+  if (row < rows) {
+    float a[8], b[8];
+    load8f(o + row * 64 + part * 8, a);
+    load8f(dout + row * 64 + part * 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += a[e] * b[e];
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) dvec[row] = acc;
 }
 
 // ---------------------------------------------------------- dQ / dK finish
@@ -693,7 +724,7 @@ hipError_t launch_rowkey(int dtype, const RowKeyArgs& a, int BH, hipStream_t s) 
 
 hipError_t launch_rowdot(int dtype, int out_f32, const void* o, const void* dout, float* dvec,
                          int64_t rows, hipStream_t s) {
-  dim3 grid(nblk(rows, 256));
+  dim3 grid(nblk(rows * 8, 256));
   if (dtype == 0 && out_f32)
     hipLaunchKernelGGL((rowdot_kernel<float, float>), grid, dim3(256), 0, s,
                        reinterpret_cast<const float*>(o), reinterpret_cast<const float*>(dout), dvec, rows);
