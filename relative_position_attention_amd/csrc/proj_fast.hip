@@ -12,6 +12,15 @@
 // multiplied, then put into LDS (double buffered), where the four waves read
 // them as MFMA B operands.  Workgroups are ordered widest group first, which
 // balances the jagged windows of causal identity maps.
+//
+// Stores.  A row of Z starts at an arbitrary element (rows are packed at a
+// pitch of 7 or 1 mod 8), so the results of a middle tile go through LDS:
+// each row's 64 values are written shifted by the row's misalignment m, and
+// threads store whole aligned 16-byte chunks (eight per row and tile instead
+// of 64 2-byte stores).  The chunk that runs into the next tile (the row's
+// last m values) is carried over in LDS and stored with the next tile's
+// first chunk.  The first and the last tile of a row store their entries one
+// by one, as does the carried part that the last tile takes over.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -20,10 +29,13 @@ namespace relpos {
 namespace {
 
 constexpr int kTP = 72;  // LDS pitch of a table tile (bf16), 144-byte rows
+constexpr int kZT = 88;  // LDS pitch of the staged result tile (fp16): 64 + 8 + carry room
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   __shared__ __attribute__((aligned(16))) bf16 st[2][64 * kTP];
   __shared__ float sb[2][64];
+  __shared__ __attribute__((aligned(16))) _Float16 zt[64 * kZT];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.x;
   const int rb = nrb - 1 - static_cast<int>(blockIdx.y);
@@ -74,44 +86,119 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   const Rsrc rz = make_rsrc(reinterpret_cast<_Float16*>(p.z) + static_cast<int64_t>(bh) * p.z_bh,
                             static_cast<uint64_t>(p.z_bh) * 2);
   const int nct = (gi.pitch + 63) / 64;
-  load_tab(0);
-  store_tab(0);
-  wait_vm_all();
-  __syncthreads();
-  for (int t = 0; t < nct; ++t) {
-    const int buf = t & 1;
-    const int c0 = t * 64;
-    load_tab(c0 + 64);
-    floatx4 acc[4];
+  const int g0 = grp * kGroup;
+
+  // MFMA tile of columns c0 .. c0+63 (lane: rows rw + 4g + e, column 16 cb +
+  // c16), bias added, as fp32
+  auto tile_products = [&](int buf, float (&val)[4][4]) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 bfr =
             *reinterpret_cast<const bf16x8*>(&st[buf][(16 * cb + c16) * kTP + 32 * c + 8 * g]);
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[c], bfr, acc[cb], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[c], bfr, acc, 0, 0, 0);
       }
+      const float add = sb[buf][16 * cb + c16];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[cb][e] = acc[e] + add;
     }
-    // lane holds rows rw + 4g + e, column c0 + 16 cb + c16 (entries past the
-    // row's window or past N are dropped by the buffer range check)
+  };
+  // entries one by one (entries past the row's pitch or past N are dropped
+  // by the buffer range check)
+  auto store_each = [&](int c0, const float (&val)[4][4]) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int cl = 16 * cb + c16;
-      const int col = c0 + cl;
-      const float add = sb[buf][cl];
+      const int col = c0 + 16 * cb + c16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = rw + 4 * g + e;
         const bool ok = col < gi.pitch && i < p.N;
-        const uint32_t off = ok ? static_cast<uint32_t>(gi.base + (i - grp * kGroup) * gi.pitch + col) * 2 : kOob;
-        const _Float16 v = from_f<_Float16>(acc[cb][e] + add);
+        const uint32_t off = ok ? static_cast<uint32_t>(gi.base + (i - g0) * gi.pitch + col) * 2 : kOob;
+        const _Float16 v = from_f<_Float16>(val[cb][e]);
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rz, off, 0, 0);
       }
     }
+  };
+  // the tile into LDS, row r at columns c + m(r) (+ the carry in front)
+  int mis[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) mis[e] = (gi.base + (rw + 4 * g + e - g0) * gi.pitch) & 7;
+  auto put_lds = [&](const float (&val)[4][4]) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wave + 4 * g + e;
+        zt[r * kZT + 16 * cb + c16 + mis[e]] = from_f<_Float16>(val[cb][e]);
+      }
+  };
+  // thread (row zr, quarter zq) stores chunks zq and zq + 4 of its row, and
+  // quarter 0 moves the carried chunk (LDS columns 64 .. 71) to the front
+  const int zr = tid >> 2, zq = tid & 3;
+  const int zi = r0 + zr;
+  const int zm = (gi.base + (zi - g0) * gi.pitch) & 7;
+  const int zstart = gi.base + (zi - g0) * gi.pitch - zm;  // aligned chunk base
+  auto store_chunks = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = zq + 4 * u;
+      const uint4 w = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 8 * k]);
+      const uint32_t off = zi < p.N ? static_cast<uint32_t>(zstart + c0 + 8 * k) * 2 : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w), rz, off, 0, 0);
+    }
+    if (zq == 0)
+      *reinterpret_cast<uint4*>(&zt[zr * kZT]) = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 64]);
+  };
+
+  load_tab(0);
+  store_tab(0);
+  wait_vm_all();
+  __syncthreads();
+  float val[4][4];
+  // first tile: entries one by one, and into LDS for the carry
+  load_tab(64);
+  tile_products(0, val);
+  store_each(0, val);
+  if (nct > 2) put_lds(val);
+  store_tab(1);
+  __syncthreads();
+  if (nct > 2) {
+    if (zq == 0)
+      *reinterpret_cast<uint4*>(&zt[zr * kZT]) = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 64]);
+    __syncthreads();
+  }
+  // middle tiles: aligned 16-byte chunks
+  for (int t = 1; t + 1 < nct; ++t) {
+    const int buf = t & 1;
+    const int c0 = t * 64;
+    load_tab(c0 + 64);
+    tile_products(buf, val);
+    put_lds(val);
+    __syncthreads();
+    store_chunks(c0);
     // (the tile after the last is staged too, into the buffer no one reads)
     store_tab(buf ^ 1);
     __syncthreads();
+  }
+  // last tile: entries one by one, and the carried entries of the tile before
+  // (LDS columns 0 .. m - 1) when that tile stored chunks
+  if (nct > 1) {
+    const int t = nct - 1;
+    tile_products(t & 1, val);
+    store_each(t * 64, val);
+    if (nct > 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = zq + 4 * u;  // carried entry k of row zr (k < m)
+        const int col = t * 64 - zm + k;
+        const bool ok = k < zm && zi < p.N;
+        const uint32_t off = ok ? static_cast<uint32_t>(zstart + t * 64 + k) * 2 : kOob;
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, zt[zr * kZT + k]), rz, off, 0, 0);
+        (void)col;
+      }
+    }
   }
 }
 
