@@ -105,6 +105,30 @@ def reduction_bytes(spec, delta):
             tok + k_reads * B * H * k_entries * 2)
 
 
+def measured_stage_traffic(stage):
+    """HBM bytes per call of a reduction stage, e.g. "query reduction (txl)",
+    from the committed rocprofv3 counter summary
+    (profiles/traffic_reductions_n8192.json), if it was taken on the current
+    reduction sources; else None."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "relative_position_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in [os.path.join(csrc, "reduce_fast.hip"), os.path.join(csrc, "aux.hip")] + \
+            sorted(glob.glob(os.path.join(csrc, "*.hpp"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    path = os.path.join(ROOT, "profiles", "traffic_reductions_n8192.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    st = rec.get("stages", {}).get(stage)
+    return st["hbm_bytes_per_call"] if st else None
+
+
 # Algorithmic MFMA work of each attention kernel, in N x N x d products:
 # forward QK^T, PV; query pass QK^T, dO V^T, dS K; key pass QK^T, dO V^T,
 # P^T dO, dS^T Q (the operand splits for peaked softmax are not counted).
@@ -342,7 +366,11 @@ def main():
            "kernels": "finalize + partials + fold (+ bias / v / u sums)",
            "avg_ms": round(red_ms, 4), "bytes_per_call": red_b,
            "achieved": round(red_b / red_ms / 1e6, 1), "peak": MI355X_HBM_GBPS,
-           "unit": "GB/s", "frac": round(red_b / red_ms / 1e6 / MI355X_HBM_GBPS, 4)}
+           "unit": "GB/s", "frac": round(red_b / red_ms / 1e6 / MI355X_HBM_GBPS, 4),
+           "traffic": measured_stage_traffic(f"{red_stage} ({red_run.name})")}
+    if hbm["traffic"] is not None:
+        hbm["traffic_unit"] = "bytes per call (rocprofv3 FETCH_SIZE, WRITE_SIZE, copy-calibrated)"
+        hbm["traffic_gbps"] = round(hbm["traffic"] / red_ms / 1e6, 1)
 
     value = step_flops / ms_per_step / 1e9
     out = {
