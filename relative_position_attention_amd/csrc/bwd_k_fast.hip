@@ -14,7 +14,12 @@
 //   P = exp2(S tau log2 e - L log2 e), G' = P (dP - D) (G = tau G'; tau
 //   multiplies the finished sums instead);
 //   dV^T += dO^T P and dK^T += Q^T G' on MFMA (dO^T and Q^T read with the
-//   transposing LDS read; P and G' as bf16, or bf16 hi + lo under F_SPLIT).
+//   transposing LDS read; P and G' as bf16).  Under F_SPLIT (a strongly
+//   peaked softmax) G' enters dK as a bf16 pair hi + lo (~16 significant
+//   bits) and P enters dV as fp16 (11 bits, against dO and, for dP, V
+//   converted to fp16 when staged): an 11-bit P moves dV by ~2^-12 |dO|,
+//   well inside the tolerance, where an 8-bit one does not, and costs one
+//   product instead of the pair's two.
 // Key offset gradients ([RPA] §4.2): a band pair writes G to
 // dZ~^K[j, delta + D] (single writer, aligned 4-entry runs); pairs with
 // |delta| >= D add into two fp32 per-key boundary sums; with the
@@ -33,6 +38,8 @@ template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int total, int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
+  // fp16 P in dV = P^T dO (under F_SPLIT): dO and V as fp16 words
+  constexpr bool HP = SPLIT;
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     for (int c = 0; c < 2; ++c) {
       const uint32_t off = static_cast<uint32_t>(j * 128 + 64 * c + 16 * g);
       kf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rk, off));
-      vf[kb][c] = __builtin_bit_cast(bf16x8, bload16(rv, off));
+      vf[kb][c] = __builtin_bit_cast(bf16x8, stage16<HP>(bload16(rv, off)));
     }
     const bool ok = j < N && kon[kb];
     klo[kb] = (KC && ok) ? a.keylo[tok + j] : 0.f;
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   };
   auto store_tile = [&](const TileRegs& r, int buf, int i0) {
     *reinterpret_cast<uint4*>(&sq[buf][kr * kP + kc8]) = r.q;
-    *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = r.d;
+    *reinterpret_cast<uint4*>(&sd[buf][kr * kP + kc8]) = stage16<HP>(r.d);
     // L enters log2 units; padding rows get L = inf (P = 0) and zeros
     const bool ok = i0 + sqi < N;
     const float v = sx == 0 ? (ok ? r.st * kLog2e : INFINITY) : (ok ? r.st : 0.f);
@@ -308,10 +315,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
           const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + c16) * kP + 32 * c + 8 * g);
           const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + (16 * qb + c16) * kP + 32 * c + 8 * g);
           s[qb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[0][c], s[qb][0], 0, 0, 0);
-          dp[qb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[0][c], dp[qb][0], 0, 0, 0);
+          dp[qb][0] = mma16<HP>(da, vf[0][c], dp[qb][0]);
           if (both) {
             s[qb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[1][c], s[qb][1], 0, 0, 0);
-            dp[qb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[1][c], dp[qb][1], 0, 0, 0);
+            dp[qb][1] = mma16<HP>(da, vf[1][c], dp[qb][1]);
           }
         }
       }
@@ -498,19 +505,16 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       // dV^T += dO^T P ; dK^T += Q^T G  (K axis: the tile's 32 queries, in the
       // order 4g + e, 16 + 4g + e of the lanes' own values)
       {
-        bf16x8 pf[2], pl[2], gf[2], gl[2];
+        bf16x8 pf[2], gf[2], gl[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float x = s[e >> 2][kb][e & 3];
             const float y = dp[e >> 2][kb][e & 3];
-            pf[kb][e] = static_cast<bf16>(x);
+            pf[kb][e] = op16<HP>(x);
             gf[kb][e] = static_cast<bf16>(y);
-            if (SPLIT) {
-              pl[kb][e] = static_cast<bf16>(x - static_cast<float>(pf[kb][e]));
-              gl[kb][e] = static_cast<bf16>(y - static_cast<float>(gf[kb][e]));
-            }
+            if (SPLIT) gl[kb][e] = static_cast<bf16>(y - static_cast<float>(gf[kb][e]));
           }
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
@@ -529,12 +533,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             if (kb == 1 && !both) continue;
-            dv[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt8, pf[kb], dv[kb][db], 0, 0, 0);
+            dv[kb][db] = mma16<HP>(dt8, pf[kb], dv[kb][db]);
             dk[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt8, gf[kb], dk[kb][db], 0, 0, 0);
-            if (SPLIT) {
-              dv[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dt8, pl[kb], dv[kb][db], 0, 0, 0);
+            if (SPLIT)
               dk[kb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt8, gl[kb], dk[kb][db], 0, 0, 0);
-            }
           }
         }
       }

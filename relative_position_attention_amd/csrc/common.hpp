@@ -193,6 +193,52 @@ __device__ __forceinline__ bf16x4 lds_tr4(const bf16* tile, int pitch, int row0,
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- fp16 operands.  fp16 and bf16 words are both 16-bit, so a tile keeps
+// its LDS layout and a fragment its registers whichever it holds: the words
+// are converted when a tile is staged, and mma16<H> picks the instruction.
+// fp16 keeps 11 significant bits against bf16's 8.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+// Eight bf16 values as fp16 (round to nearest even, clamped to +-65504).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = __builtin_amdgcn_fmed3f(__uint_as_float(in[k] << 16), -65504.f, 65504.f);
+    const float b = __builtin_amdgcn_fmed3f(__uint_as_float(in[k] & 0xffff0000u), -65504.f, 65504.f);
+    const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
+    out[k] = static_cast<uint32_t>(__builtin_bit_cast(u16, ha)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(u16, hb)) << 16);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+template <bool H>
+__device__ __forceinline__ uint4 stage16(uint4 v) {
+  if constexpr (H)
+    return bf16x8_to_f16x8(v);
+  else
+    return v;
+}
+// a 16-bit MFMA over bf16-typed fragments holding bf16 (H = false) or fp16
+// (H = true) words
+template <bool H>
+__device__ __forceinline__ floatx4 mma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  if constexpr (H)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                  __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// an fp32 value as a 16-bit operand word (round to nearest even)
+template <bool H>
+__device__ __forceinline__ bf16 op16(float x) {
+  if constexpr (H)
+    return __builtin_bit_cast(bf16, static_cast<_Float16>(x));
+  else
+    return static_cast<bf16>(x);
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: everything derived from it stays in scalar registers, so branches on
 // it are scalar branches.  (Derived from the lane id alone, the compiler
