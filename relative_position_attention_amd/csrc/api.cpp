@@ -167,8 +167,9 @@ int build_groups(const Plan& p, void* z, hipStream_t s) {
   return RELPOS_OK;
 }
 
-// Expanded row maps and fold intervals, built on the device into ws.
-int build_maps(const Plan& p, void* ws, hipStream_t s) {
+// Expanded row maps and (with_fold: only the backward's table-gradient folds
+// read them) fold intervals, built on the device into ws.
+int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
   struct Tab {
     bool on;
     const std::vector<int32_t>* beta;
@@ -205,8 +206,10 @@ int build_maps(const Plan& p, void* ws, hipStream_t s) {
         RP_HIP(launch_meta_fill(c, s));
       }
     }
-    int32_t* fold = at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(t.fold_idx) * R * 2;
-    RP_HIP(launch_fold_meta(beta, fold, p.S, R, s));
+    if (with_fold) {
+      int32_t* fold = at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(t.fold_idx) * R * 2;
+      RP_HIP(launch_fold_meta(beta, fold, p.S, R, s));
+    }
   }
   return RELPOS_OK;
 }
@@ -377,7 +380,7 @@ int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos
     return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
   if (!aligned16(z) || !aligned16(ws)) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
   if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
-  if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = build_maps(p, ws, s, false)) != RELPOS_OK) return rc;
   if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
   return project_into(p, desc, in, z, ws, s);
 }
@@ -404,7 +407,7 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (z == nullptr) {
     z = at_off<char>(ws, p.ws_fwd_end);
     if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
-    if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
+    if ((rc = build_maps(p, ws, s, false)) != RELPOS_OK) return rc;
     if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
     if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   }
@@ -444,7 +447,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (!aligned16(ws) || (z && !aligned16(z))) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
 
   const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
-  if ((rc = build_maps(p, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = build_maps(p, ws, s, true)) != RELPOS_OK) return rc;
   if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
   if (z == nullptr) {
     z = at_off<char>(ws, p.ws_bwd_end);

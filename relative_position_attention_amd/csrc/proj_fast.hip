@@ -67,20 +67,26 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   // out-of-range buffer offsets for entries past the window), so each wave
   // issues the same memory instructions on every path: the wait for the next
   // table tile then never covers the stores still in flight.
+  // Table tiles are requested two tiles ahead, into two register sets that
+  // alternate (the tile loop is unrolled twice so each set keeps its role):
+  // a tile's loads then have two tiles of work to arrive in.
   const int ar = tid >> 2, ac = (tid & 3) * 16;
-  uint4 ta[2];
-  float tb = 0.f;
-  auto load_tab = [&](int c0) {
+  struct TabRegs {
+    uint4 a[2];
+    float b;
+  };
+  TabRegs ra0, ra1;
+  auto load_tab = [&](TabRegs& R, int c0) {
     const int s = iclamp(c0 + ar - gi.pad + gi.slo, 0, D2);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) ta[u] = bload16(ra, static_cast<uint32_t>(s * 128 + (ac + 8 * u) * 2));
+    for (int u = 0; u < 2; ++u) R.a[u] = bload16(ra, static_cast<uint32_t>(s * 128 + (ac + 8 * u) * 2));
     const int sc = iclamp(c0 + (tid & 63) - gi.pad + gi.slo, 0, D2);
-    tb = bloadf(rbt, static_cast<uint32_t>(sc) * 4);
+    R.b = bloadf(rbt, static_cast<uint32_t>(sc) * 4);
   };
-  auto store_tab = [&](int buf) {
+  auto store_tab = [&](const TabRegs& R, int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&st[buf][ar * kTP + ac + 8 * u]) = ta[u];
-    if (tid < 64) sb[buf][tid] = tb;
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&st[buf][ar * kTP + ac + 8 * u]) = R.a[u];
+    if (tid < 64) sb[buf][tid] = R.b;
   };
 
   const Rsrc rz = make_rsrc(reinterpret_cast<_Float16*>(p.z) + static_cast<int64_t>(bh) * p.z_bh,
@@ -152,40 +158,50 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
       *reinterpret_cast<uint4*>(&zt[zr * kZT]) = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 64]);
   };
 
-  load_tab(0);
-  store_tab(0);
+  load_tab(ra0, 0);
+  store_tab(ra0, 0);
   wait_vm_all();
   __syncthreads();
+  load_tab(ra1, 64);
   float val[4][4];
   // first tile: entries one by one, and into LDS for the carry
-  load_tab(64);
+  load_tab(ra0, 128);
   tile_products(0, val);
   store_each(0, val);
   if (nct > 2) put_lds(val);
-  store_tab(1);
+  store_tab(ra1, 1);
   __syncthreads();
   if (nct > 2) {
     if (zq == 0)
       *reinterpret_cast<uint4*>(&zt[zr * kZT]) = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 64]);
     __syncthreads();
   }
-  // middle tiles: aligned 16-byte chunks
-  for (int t = 1; t + 1 < nct; ++t) {
+  // middle tiles: aligned 16-byte chunks.  Tile t + 1 sits in the set loaded
+  // during tile t - 1, and tile t + 2 goes into the other one (tiles past the
+  // window read clamped rows, staged into the buffer no one reads)
+  auto middle = [&](int t, TabRegs& next2, const TabRegs& next1) {
     const int buf = t & 1;
     const int c0 = t * 64;
-    load_tab(c0 + 64);
+    load_tab(next2, c0 + 128);
     tile_products(buf, val);
     put_lds(val);
     __syncthreads();
     store_chunks(c0);
-    // (the tile after the last is staged too, into the buffer no one reads)
-    store_tab(buf ^ 1);
+    store_tab(next1, buf ^ 1);
     __syncthreads();
+  };
+  int t = 1;
+  for (;;) {
+    if (t + 1 >= nct) break;
+    middle(t, ra1, ra0);
+    ++t;
+    if (t + 1 >= nct) break;
+    middle(t, ra0, ra1);
+    ++t;
   }
   // last tile: entries one by one, and the carried entries of the tile before
   // (LDS columns 0 .. m - 1) when that tile stored chunks
   if (nct > 1) {
-    const int t = nct - 1;
     tile_products(t & 1, val);
     store_each(t * 64, val);
     if (nct > 2) {
