@@ -37,11 +37,12 @@ constexpr int kSP = 76;   // LDS pitch of the row-shifted fp32 dZ~ tiles
 // alignment: entry s0 + p of token row r sits at zf[r][p + so[r]], so[r] =
 // e0 mod VEC.  Entries outside the token's reachable band rows
 // [max(smin, 1), min(smax, 2D-1)] are written as zero.  Thread t moves token
-// row t / 4, chunks t % 4, t % 4 + 4, ...
-template <typename GT>
+// row t / 4, chunks t % 4, t % 4 + 4, ...  W > 1: 64 W entries per token
+// row (rows s0 .. s0 + 64 W - 1), LDS pitch SP.
+template <typename GT, int W = 1, int SP = kSP>
 struct DzTile {
   static constexpr int VEC = 16 / sizeof(GT);
-  static constexpr int NCH = 64 / VEC + 1;  // aligned chunks covering 64 entries
+  static constexpr int NCH = 64 * W / VEC + 1;  // aligned chunks covering 64 W entries
   static constexpr int PER = (NCH + 3) / 4;
   uint4 w[PER];
   int e0;      // element index of s0 in the token's row
@@ -66,7 +67,7 @@ struct DzTile {
     for (int u = 0; u < PER; ++u) {
       const int ch = tq + 4 * u;
       const int ce = cf + ch * VEC;
-      const bool ok = ch < NCH && ce >= 0 && ce <= e0 + 63 && hi >= 0 && lo <= 63 && lo <= hi;
+      const bool ok = ch < NCH && ce >= 0 && ce <= e0 + 64 * W - 1 && hi >= 0 && lo <= 64 * W - 1 && lo <= hi;
       w[u] = bload16(rz, ok ? static_cast<uint32_t>(ce) * sizeof(GT) : kOob);
     }
   }
@@ -103,7 +104,7 @@ struct DzTile {
       }
 #pragma unroll
       for (int k = 0; k < VEC / 4; ++k)
-        *reinterpret_cast<floatx4*>(&zf[r * kSP + VEC * ch + 4 * k]) =
+        *reinterpret_cast<floatx4*>(&zf[r * SP + VEC * ch + 4 * k]) =
             floatx4{f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]};
     }
   }
@@ -235,20 +236,25 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
 }
 // ---------------------------------------------------------------- partials
 
-template <typename GT>
+// W: 64-row tiles of s per workgroup.  A token row's run of 64 W entries
+// starts at an arbitrary element, so it touches about 64 W / 64 + 1 cache
+// lines of 64 entries: two tiles per stage read three lines where two
+// workgroups of one tile each read four.
+template <typename GT, int W>
 __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
-  __shared__ __attribute__((aligned(16))) float zf[64 * kSP];  // [token][s + shift]
+  constexpr int SP = 64 * W + 12;  // LDS pitch of the row-shifted fp32 tile
+  __shared__ __attribute__((aligned(16))) float zf[64 * SP];   // [token][s + shift]
   __shared__ __attribute__((aligned(16))) int so[64];
   __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];   // [token][d]
   __shared__ float bsh[2][64];
-  __shared__ float p2red[4][64];
+  __shared__ float p2red[4][64 * W];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int D = p.D;
   // s tiles from the one holding offset 0 (s = D) outwards: those reach the
   // most tokens, so the longest blocks start first
   int tile;
   {
-    const int T = static_cast<int>(gridDim.x), c = imin(D / 64, T - 1);
+    const int T = static_cast<int>(gridDim.x), c = imin(D / (64 * W), T - 1);
     const int below = c, above = T - 1 - c, mm = imin(below, above);
     const int k = static_cast<int>(blockIdx.x) - 1;
     if (k < 0)
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
     else
       tile = above > below ? c + mm + 1 + (k - 2 * mm) : c - mm - 1 - (k - 2 * mm);
   }
-  const int s0 = tile * 64;
+  const int s0 = tile * 64 * W;
   const int h = blockIdx.y;
   const int chunk = blockIdx.z;
   const int nrb = (p.N + 63) / 64;
@@ -266,14 +272,18 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   const int per = (total + p.nchunk - 1) / p.nchunk;
   const int sb0 = chunk * per, sb1 = imin(total, sb0 + per);
   const bool has0 = s0 == 0;
-  const bool has2 = (2 * D >= s0) && (2 * D < s0 + 64);
+  const bool has2 = (2 * D >= s0) && (2 * D < s0 + 64 * W);
   const bool want_p1 = p.p1 != nullptr;
   const bool want_p2 = p.p2 != nullptr;
 
-  floatx4 acc[4];
+  floatx4 acc[W][4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float p2acc = 0.f;           // thread (s = tid & 63, quarter tid >> 6)
+  for (int st = 0; st < W; ++st)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[st][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float p2acc[W];              // thread (s = 64 st + (tid & 63), quarter tid >> 6)
+#pragma unroll
+  for (int st = 0; st < W; ++st) p2acc[st] = 0.f;
   float bx0 = 0.f, bx1 = 0.f;  // boundary P1 (threads < 64: d = tid)
   float bs0 = 0.f, bs1 = 0.f;  // boundary P2 (every thread < 64, same order)
 
@@ -286,14 +296,14 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
     else
       query_group_window(grp, p.N, D, p.causal != 0, slo, shi);
     const int sa = imax(1, slo), se = imin(2 * D - 1, shi);
-    return D >= 1 && sa <= se && s0 <= se && s0 + 63 >= sa;
+    return D >= 1 && sa <= se && s0 <= se && s0 + 64 * W - 1 >= sa;
   };
   auto next_stage = [&](int sb) {
     while (sb < sb1 && !(has0 || has2 || band_hit(sb))) ++sb;
     return sb;
   };
 
-  DzTile<GT> dt;
+  DzTile<GT, W, SP> dt;
   uint4 tx[2];
   float tb[2] = {0.f, 0.f};
   bool hit_next = false;
@@ -345,39 +355,48 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
         // the order 32c + 4g + e, 32c + 16 + 4g + e
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const int sc = 16 * wave + c16;
           const int t0 = 32 * c + 4 * g;
           const int4 oa = *reinterpret_cast<const int4*>(&so[t0]);
           const int4 ob = *reinterpret_cast<const int4*>(&so[t0 + 16]);
           const int oo[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = zf[(t0 + e) * kSP + oo[e] + sc];
-            v[e + 4] = zf[(t0 + 16 + e) * kSP + oo[e + 4] + sc];
-          }
-          const bf16x8 a8 = pack_bf16x8(v);
+          bf16x8 b8[4];
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const bf16x4 blo = lds_tr4(xt, kRP, 32 * c + 4 * g, 16 * db, c16);
             const bf16x4 bhi = lds_tr4(xt, kRP, 32 * c + 16 + 4 * g, 16 * db, c16);
-            bf16x8 b8;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              b8[e] = blo[e];
-              b8[e + 4] = bhi[e];
+              b8[db][e] = blo[e];
+              b8[db][e + 4] = bhi[e];
             }
-            acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc[db], 0, 0, 0);
+          }
+#pragma unroll
+          for (int st = 0; st < W; ++st) {
+            const int sc = 64 * st + 16 * wave + c16;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = zf[(t0 + e) * SP + oo[e] + sc];
+              v[e + 4] = zf[(t0 + 16 + e) * SP + oo[e + 4] + sc];
+            }
+            const bf16x8 a8 = pack_bf16x8(v);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+              acc[st][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8[db], acc[st][db], 0, 0, 0);
           }
         }
       }
       if (want_p2) {
-        // column s = tid & 63, tokens 16 (tid >> 6) .. +15, in order
-        const int s = tid & 63, q = tid >> 6;
-        float part = 0.f;
+        // columns s = 64 st + (tid & 63), tokens 16 (tid >> 6) .. +15, in order
+        const int q = tid >> 6;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part += zf[(16 * q + e) * kSP + so[16 * q + e] + s];
-        p2acc += part;
+        for (int st = 0; st < W; ++st) {
+          const int s = 64 * st + (tid & 63);
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) part += zf[(16 * q + e) * SP + so[16 * q + e] + s];
+          p2acc[st] += part;
+        }
       }
     }
     if (has0 || has2) {
@@ -405,12 +424,14 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   const int64_t pbase = (static_cast<int64_t>(h) * p.nchunk + chunk) * p.S;
   if (want_p1) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int s = s0 + 16 * wave + 4 * g + t;
-      if (s >= p.S) continue;
+    for (int st = 0; st < W; ++st)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) p.p1[(pbase + s) * 64 + 16 * db + c16] = acc[db][t];
-    }
+      for (int t = 0; t < 4; ++t) {
+        const int s = s0 + 64 * st + 16 * wave + 4 * g + t;
+        if (s >= p.S) continue;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) p.p1[(pbase + s) * 64 + 16 * db + c16] = acc[st][db][t];
+      }
     __syncthreads();
     if (tid < 64) {
       // boundary rows: added in a fixed order after the band part
@@ -419,15 +440,20 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
     }
   }
   if (want_p2) {
-    p2red[tid >> 6][tid & 63] = p2acc;
+#pragma unroll
+    for (int st = 0; st < W; ++st) p2red[tid >> 6][64 * st + (tid & 63)] = p2acc[st];
     __syncthreads();
     if (tid < 64) {
-      const int s = s0 + tid;
-      if (s < p.S) {
-        float v = ((p2red[0][tid] + p2red[1][tid]) + p2red[2][tid]) + p2red[3][tid];
-        if (has0 && s == 0) v += bs0 + (2 * D == 0 ? bs1 : 0.f);
-        if (has2 && D > 0 && s == 2 * D) v += bs1;
-        p.p2[pbase + s] = v;
+#pragma unroll
+      for (int st = 0; st < W; ++st) {
+        const int sl = 64 * st + tid;
+        const int s = s0 + sl;
+        if (s < p.S) {
+          float v = ((p2red[0][sl] + p2red[1][sl]) + p2red[2][sl]) + p2red[3][sl];
+          if (has0 && s == 0) v += bs0 + (2 * D == 0 ? bs1 : 0.f);
+          if (has2 && D > 0 && s == 2 * D) v += bs1;
+          p.p2[pbase + s] = v;
+        }
       }
     }
   }
@@ -450,13 +476,13 @@ hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s) {
 }
 
 hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s) {
-  dim3 grid(nblk(p.S, 64), p.H, p.nchunk);
+  // 16-bit entries: two 64-row tiles of s per workgroup
   if (p.dz_f32)
-    hipLaunchKernelGGL((partials_fast<float>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((partials_fast<float, 1>), dim3(nblk(p.S, 64), p.H, p.nchunk), dim3(256), 0, s, p);
   else if (p.dz_f16)
-    hipLaunchKernelGGL((partials_fast<_Float16>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((partials_fast<_Float16, 2>), dim3(nblk(p.S, 128), p.H, p.nchunk), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((partials_fast<bf16>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((partials_fast<bf16, 2>), dim3(nblk(p.S, 128), p.H, p.nchunk), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
