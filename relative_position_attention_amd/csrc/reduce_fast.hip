@@ -119,11 +119,14 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
 
 // ---------------------------------------------------------------- finalize
 
-template <typename GT>
+// W: stages of 64 W expanded rows (see partials_fast for why wider runs
+// fetch fewer lines per entry)
+template <typename GT, int W>
 __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
-  __shared__ __attribute__((aligned(16))) float zf[64 * kSP];
+  constexpr int SP = 64 * W + 12;
+  __shared__ __attribute__((aligned(16))) float zf[64 * SP];
   __shared__ int so[64];
-  __shared__ __attribute__((aligned(16))) bf16 at[64 * kRP];
+  __shared__ __attribute__((aligned(16))) bf16 at[64 * W * kRP];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.y;
   const int h = bh % f.H;
@@ -152,26 +155,27 @@ __global__ __launch_bounds__(256) void finalize_fast(FinalizeArgs f) {
       const Rsrc ra = make_rsrc(atab, static_cast<uint64_t>(f.S) * 128);
       // A~ rows s0 .. s0+63, row-major (rows past the table read zero)
       const int ar = tid >> 2, ac = (tid & 3) * 16;
-      DzTile<GT> dt;
-      uint4 ta[2];
+      DzTile<GT, W, SP> dt;
+      uint4 ta[2 * W];
       auto load_stage = [&](int s0) {
         dt.load(rz, gi, grp * kGroup, r0, s0, f.N, D, f.key_side != 0, f.causal != 0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          ta[u] = bload16(ra, static_cast<uint32_t>((s0 + ar) * 128 + (ac + 8 * u) * 2));
+        for (int u = 0; u < 2 * W; ++u)
+          ta[u] = bload16(ra, static_cast<uint32_t>((s0 + ar + 64 * (u >> 1)) * 128 + (ac + 8 * (u & 1)) * 2));
       };
       if (sa <= sb) load_stage(sa);
-      for (int s0 = sa; s0 <= sb; s0 += 64) {
+      for (int s0 = sa; s0 <= sb; s0 += 64 * W) {
         dt.store(zf, so);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) *reinterpret_cast<uint4*>(&at[ar * kRP + ac + 8 * u]) = ta[u];
+        for (int u = 0; u < 2 * W; ++u)
+          *reinterpret_cast<uint4*>(&at[(ar + 64 * (u >> 1)) * kRP + ac + 8 * (u & 1)]) = ta[u];
         __syncthreads();
-        if (s0 + 64 <= sb) load_stage(s0 + 64);
+        if (s0 + 64 * W <= sb) load_stage(s0 + 64 * W);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 2 * W; ++c) {
           // K axis (rows s) in the order 32c + 4g + e, 32c + 16 + 4g + e
           const int tr = 16 * wave + c16;
-          const float* zr = zf + tr * kSP + so[tr] + 32 * c + 4 * g;
+          const float* zr = zf + tr * SP + so[tr] + 32 * c + 4 * g;
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -466,12 +470,16 @@ inline unsigned nblk(int64_t n, int b) { return static_cast<unsigned>((n + b - 1
 hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s) {
   const unsigned nrb = nblk(f.N, 64);
   dim3 grid(f.causal ? (nrb + 1) / 2 : nrb, BH);
+  // fp16 entries (the causal Transformer-XL query side: few workgroups, long
+  // rows) take stages of two 64-row tiles; bf16 entries keep one, where the
+  // occupancy of the wider stage (3 workgroups per CU instead of 5) costs more
+  // than its fewer cache lines save
   if (f.dz_f32)
-    hipLaunchKernelGGL((finalize_fast<float>), grid, dim3(256), 0, s, f);
+    hipLaunchKernelGGL((finalize_fast<float, 1>), grid, dim3(256), 0, s, f);
   else if (f.dz_f16)
-    hipLaunchKernelGGL((finalize_fast<_Float16>), grid, dim3(256), 0, s, f);
+    hipLaunchKernelGGL((finalize_fast<_Float16, 2>), grid, dim3(256), 0, s, f);
   else
-    hipLaunchKernelGGL((finalize_fast<bf16>), grid, dim3(256), 0, s, f);
+    hipLaunchKernelGGL((finalize_fast<bf16, 1>), grid, dim3(256), 0, s, f);
   return hipGetLastError();
 }
 
