@@ -562,26 +562,42 @@ __global__ __launch_bounds__(256) void partials_kernel(PartialArgs p) {
 }
 
 // Fixed-order sums over chunks (and heads for a shared table) of the
-// partials, then the bucket fold over the table row's expanded rows.
-__global__ __launch_bounds__(64) void fold_table_kernel(FoldArgs f, int dtype) {
-  const int r = blockIdx.x, ht = blockIdx.y, d = threadIdx.x;
+// partials, then the bucket fold over the table row's expanded rows.  The
+// row's items (s, h, c), in that nesting order, are dealt round robin to the
+// four waves (four loads in flight each); the four wave sums are added in
+// wave order, so the result is the same on every call.
+__global__ __launch_bounds__(256) void fold_table_kernel(FoldArgs f, int dtype) {
+  __shared__ float red[4][64];
+  const int r = blockIdx.x, ht = blockIdx.y, d = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int sa = f.fold[2 * r], sb = f.fold[2 * r + 1];
-  const int h0 = f.shared ? 0 : ht, h1 = f.shared ? f.H : ht + 1;
-  float sum = 0.f;
-  for (int s = sa; s <= sb; ++s)
-    for (int h = h0; h < h1; ++h) {
-      float vb = 0.f;
-      if (f.vb != nullptr)
-        vb = dtype == 0 ? reinterpret_cast<const float*>(f.vb)[h * 64 + d]
-                        : static_cast<float>(reinterpret_cast<const bf16*>(f.vb)[h * 64 + d]);
-      for (int c = 0; c < f.nchunk; ++c) {
-        const int64_t base = (static_cast<int64_t>(h) * f.nchunk + c) * f.S + s;
-        float v = f.p1[base * 64 + d];
-        if (f.vb != nullptr) v += vb * f.p2[base];
-        sum += v;
-      }
+  const int h0 = f.shared ? 0 : ht, nh = f.shared ? f.H : 1;
+  const int n = sb >= sa ? (sb - sa + 1) * nh * f.nchunk : 0;
+  auto item = [&](int it) {
+    const int c = it % f.nchunk, rest = it / f.nchunk;
+    const int h = h0 + rest % nh, s = sa + rest / nh;
+    const int64_t base = (static_cast<int64_t>(h) * f.nchunk + c) * f.S + s;
+    float v = f.p1[base * 64 + d];
+    if (f.vb != nullptr) {
+      const float vb = dtype == 0 ? reinterpret_cast<const float*>(f.vb)[h * 64 + d]
+                                  : static_cast<float>(reinterpret_cast<const bf16*>(f.vb)[h * 64 + d]);
+      v += vb * f.p2[base];
     }
-  f.out[r * f.row_stride + ht * f.head_stride + d] = sum;
+    return v;
+  };
+  float sum = 0.f;
+  int it = w;
+  for (; it + 12 < n; it += 16) {
+    const float v0 = item(it), v1 = item(it + 4), v2 = item(it + 8), v3 = item(it + 12);
+    sum += v0;
+    sum += v1;
+    sum += v2;
+    sum += v3;
+  }
+  for (; it < n; it += 4) sum += item(it);
+  red[w][d] = sum;
+  __syncthreads();
+  if (w == 0)
+    f.out[r * f.row_stride + ht * f.head_stride + d] = ((red[0][d] + red[1][d]) + red[2][d]) + red[3][d];
 }
 
 // db[h][s] = sum over chunks c (ascending) of P2[h][c][s]
@@ -763,7 +779,7 @@ hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s) {
 }
 
 hipError_t launch_fold_table(int dtype, const FoldArgs& f, hipStream_t s) {
-  hipLaunchKernelGGL(fold_table_kernel, dim3(f.R, f.Ht), dim3(64), 0, s, f, dtype);
+  hipLaunchKernelGGL(fold_table_kernel, dim3(f.R, f.Ht), dim3(256), 0, s, f, dtype);
   return hipGetLastError();
 }
 
