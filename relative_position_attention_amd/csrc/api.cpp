@@ -485,6 +485,14 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   a.bndq = bndq;
   a.bndk = bndk;
   a.colsum = colsum;
+  // A side without a table term (no A^Q; no A^K and no u) has nothing to add
+  // to its pass's dQ (dK): with fp32 outputs the pass writes the output itself
+  // and that side's finalize kernel is skipped
+  const bool out32 = p.out_dtype == RELPOS_DTYPE_F32;
+  const bool q_direct = out32 && !p.aq;
+  const bool k_direct = out32 && !p.ak && !p.u;
+  if (q_direct) a.dqacc = static_cast<float*>(gr->dq);
+  if (k_direct) a.dkacc = static_cast<float*>(gr->dk);
   const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
@@ -495,7 +503,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   else
     RP_HIP(launch_bwd_q_bf16(qflags, a, p.B, s));
   RP_MARK(2);
-  {
+  if (!q_direct) {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
     f.acc = dqacc;
@@ -594,7 +602,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   else
     RP_HIP(launch_bwd_k_bf16(kflags, a, p.B, s));
   RP_MARK(4);
-  {
+  if (!k_direct) {
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
     f.acc = dkacc;

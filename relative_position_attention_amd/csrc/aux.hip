@@ -625,47 +625,83 @@ __global__ __launch_bounds__(256) void fold_bias_kernel(FoldBiasArgs f) {
 
 constexpr int kSplit = 64;  // partial sums per head in the two-phase row sums
 
+// Both first phases give a row r (an expanded table row, or a token) to a
+// group of eight lanes holding eight consecutive columns each (16-byte
+// loads); 32 rows are in flight per step, and the 32 row sums of each
+// column are added in row-group order through LDS, so the result is the same
+// on every call.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* v) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    const float4 y = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(wd[k] << 16);
+      v[2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+    }
+  }
+}
+
+// the 32 row groups' sums of column c8 * 8 + e (threads t: c8 = t & 7,
+// group t >> 3), reduced in group order, written by threads < 64
+__device__ __forceinline__ void reduce_groups(float (&acc)[8], float* out) {
+  __shared__ float red[32][65];
+  const int t = threadIdx.x, c8 = t & 7, grp = t >> 3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[grp][c8 * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < 64) {
+    float s = 0.f;
+    for (int k = 0; k < 32; ++k) s += red[k][t];
+    out[t] = s;
+  }
+}
+
 // dv, first phase: part[h][sp][d] = sum over the rows s of split sp of
-// db[h][s] A~^Q[s][d] (fixed order: stride-4 rows per quarter, quarters summed
-// in order)
+// db[h][s] A~^Q[s][d]
 template <typename T>
 __global__ __launch_bounds__(256) void dv_part_kernel(DvArgs a) {
-  __shared__ float part[4][64];
-  const int h = blockIdx.x, sp = blockIdx.y, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int h = blockIdx.x, sp = blockIdx.y, c8 = threadIdx.x & 7, grp = threadIdx.x >> 3;
   const int per = (a.S + kSplit - 1) / kSplit;
   const int s0 = sp * per, s1 = imin(a.S, s0 + per);
   const T* at = reinterpret_cast<const T*>(a.atq) +
                 static_cast<int64_t>(a.at_shared ? 0 : h) * a.S * 64;
-  float sum = 0.f;
-  for (int s = s0 + q; s < s1; s += 4)
-    sum += a.db[static_cast<int64_t>(h) * a.S + s] * to_f(at[static_cast<int64_t>(s) * 64 + d]);
-  part[q][d] = sum;
-  __syncthreads();
-  if (q == 0)
-    a.part[(static_cast<int64_t>(h) * kSplit + sp) * 64 + d] =
-        ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = s0 + grp; s < s1; s += 32) {
+    float v[8];
+    load8(at + static_cast<int64_t>(s) * 64 + c8 * 8, v);
+    const float w = a.db[static_cast<int64_t>(h) * a.S + s];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += w * v[e];
+  }
+  reduce_groups(acc, a.part + (static_cast<int64_t>(h) * kSplit + sp) * 64);
 }
 
 // du, first phase: part[h][sp][d] = sum over the tokens (b, j) of split sp of
 // colsum[b, h, j] k[b, h, j, d]
 template <typename T>
 __global__ __launch_bounds__(256) void du_part_kernel(DuArgs a) {
-  __shared__ float part[4][64];
-  const int h = blockIdx.x, sp = blockIdx.y, d = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int h = blockIdx.x, sp = blockIdx.y, c8 = threadIdx.x & 7, grp = threadIdx.x >> 3;
   const int64_t total = static_cast<int64_t>(a.B) * a.N;
   const int64_t per = (total + kSplit - 1) / kSplit;
   const int64_t t0 = sp * per, t1 = t0 + per < total ? t0 + per : total;
-  float sum = 0.f;
-  for (int64_t t = t0 + q; t < t1; t += 4) {
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t t = t0 + grp; t < t1; t += 32) {
     const int64_t b = t / a.N, j = t % a.N;
     const int64_t row = (b * a.H + h) * a.N + j;
-    sum += a.colsum[row] * to_f(reinterpret_cast<const T*>(a.k)[row * 64 + d]);
+    float v[8];
+    load8(reinterpret_cast<const T*>(a.k) + row * 64 + c8 * 8, v);
+    const float w = a.colsum[row];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += w * v[e];
   }
-  part[q][d] = sum;
-  __syncthreads();
-  if (q == 0)
-    a.part[(static_cast<int64_t>(h) * kSplit + sp) * 64 + d] =
-        ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+  reduce_groups(acc, a.part + (static_cast<int64_t>(h) * kSplit + sp) * 64);
 }
 
 // second phase: out[h][d] = sum over splits (ascending) of part[h][sp][d]
