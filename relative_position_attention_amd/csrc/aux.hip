@@ -199,51 +199,6 @@ __global__ __launch_bounds__(256) void project_kernel(ProjectArgs p) {
   }
 }
 
-// Per-token boundary entries (fp32): the saturated rows 0 and 2D of Z^Q and
-// Z^K, with the scalar biases and the Transformer-XL u term folded in; they
-// are all that saturated tiles read ([RPA] App. B.2 saturated-tile lemma).
-template <typename T>
-__global__ __launch_bounds__(256) void rowkey_kernel(RowKeyArgs a, int64_t rows) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (row >= rows) return;
-  const int h = static_cast<int>((row / a.N) % a.H);
-  const int D2 = a.S - 1;
-  const T* q = reinterpret_cast<const T*>(a.q) + row * 64;
-  const T* k = reinterpret_cast<const T*>(a.k) + row * 64;
-  float rl = a.bt[h * a.S + 0], rh = a.bt[h * a.S + D2];
-  if (a.atq != nullptr) {
-    const T* at = reinterpret_cast<const T*>(a.atq) +
-                  static_cast<int64_t>(a.atq_shared ? 0 : h) * a.S * 64;
-    float s0 = 0.f, s1 = 0.f;
-    for (int c = 0; c < 64; ++c) {
-      const float qv = to_f(q[c]);
-      s0 += qv * to_f(at[c]);
-      s1 += qv * to_f(at[static_cast<int64_t>(D2) * 64 + c]);
-    }
-    rl += s0;
-    rh += s1;
-  }
-  float kl = 0.f, kh = 0.f, km = 0.f;
-  if (a.atk != nullptr) {
-    const T* at = reinterpret_cast<const T*>(a.atk) +
-                  static_cast<int64_t>(a.atk_shared ? 0 : h) * a.S * 64;
-    for (int c = 0; c < 64; ++c) {
-      const float kv = to_f(k[c]);
-      kl += kv * to_f(at[c]);
-      kh += kv * to_f(at[static_cast<int64_t>(D2) * 64 + c]);
-    }
-  }
-  if (a.u != nullptr) {
-    const T* u = reinterpret_cast<const T*>(a.u) + h * 64;
-    for (int c = 0; c < 64; ++c) km += to_f(u[c]) * to_f(k[c]);
-  }
-  a.rowlo[row] = rl;
-  a.rowhi[row] = rh;
-  a.keylo[row] = kl + km;
-  a.keyhi[row] = kh + km;
-  a.keymid[row] = km;
-}
-
 // D_i = <dO_i, O_i> ([RPA] Table 9 "Preprocessing")
 // Eight lanes per row, eight consecutive elements each (one or two 16-byte
 // loads per operand, so a wave reads eight whole rows); the eight partial
@@ -284,6 +239,76 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const TO* o, const T* dout,
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
   if (row < rows && part == 0) dvec[row] = acc;
+}
+
+// the sum of a value over the eight lanes of a row (fixed butterfly)
+__device__ __forceinline__ float sum8(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
+}
+
+// Per-token boundary entries (fp32): the saturated rows 0 and 2D of Z^Q and
+// Z^K, with the scalar biases and the Transformer-XL u term folded in; they
+// are all that saturated tiles read ([RPA] App. B.2 saturated-tile lemma).
+// Eight lanes per row as in rowdot, each lane's eight products summed in
+// order, then the fixed butterfly.
+template <typename T>
+__global__ __launch_bounds__(256) void rowkey_kernel(RowKeyArgs a, int64_t rows) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid >> 3;
+  const int part = static_cast<int>(gid & 7);
+  const bool ok = row < rows;
+  const int64_t rr = ok ? row : 0;
+  const int h = static_cast<int>((rr / a.N) % a.H);
+  const int D2 = a.S - 1;
+  float q[8], k[8];
+  if (a.atq != nullptr) load8f(reinterpret_cast<const T*>(a.q) + rr * 64 + part * 8, q);
+  if (a.atk != nullptr || a.u != nullptr) load8f(reinterpret_cast<const T*>(a.k) + rr * 64 + part * 8, k);
+  float s0 = 0.f, s1 = 0.f, kl = 0.f, kh = 0.f, km = 0.f;
+  if (a.atq != nullptr) {
+    const T* at = reinterpret_cast<const T*>(a.atq) +
+                  static_cast<int64_t>(a.atq_shared ? 0 : h) * a.S * 64 + part * 8;
+    float t0[8], t1[8];
+    load8f(at, t0);
+    load8f(at + static_cast<int64_t>(D2) * 64, t1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s0 += q[e] * t0[e];
+      s1 += q[e] * t1[e];
+    }
+  }
+  if (a.atk != nullptr) {
+    const T* at = reinterpret_cast<const T*>(a.atk) +
+                  static_cast<int64_t>(a.atk_shared ? 0 : h) * a.S * 64 + part * 8;
+    float t0[8], t1[8];
+    load8f(at, t0);
+    load8f(at + static_cast<int64_t>(D2) * 64, t1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kl += k[e] * t0[e];
+      kh += k[e] * t1[e];
+    }
+  }
+  if (a.u != nullptr) {
+    float uu[8];
+    load8f(reinterpret_cast<const T*>(a.u) + h * 64 + part * 8, uu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) km += uu[e] * k[e];
+  }
+  s0 = sum8(s0);
+  s1 = sum8(s1);
+  kl = sum8(kl);
+  kh = sum8(kh);
+  km = sum8(km);
+  if (ok && part == 0) {
+    a.rowlo[row] = a.bt[h * a.S + 0] + s0;
+    a.rowhi[row] = a.bt[h * a.S + D2] + s1;
+    a.keylo[row] = kl + km;
+    a.keyhi[row] = kh + km;
+    a.keymid[row] = km;
+  }
 }
 
 // ---------------------------------------------------------- dQ / dK finish
@@ -768,9 +793,9 @@ hipError_t launch_project(int dtype, const ProjectArgs& p, int BH, int max_pitch
 hipError_t launch_rowkey(int dtype, const RowKeyArgs& a, int BH, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(BH) * a.N;
   if (dtype == 0)
-    hipLaunchKernelGGL(rowkey_kernel<float>, dim3(nblk(rows, 256)), dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(rowkey_kernel<float>, dim3(nblk(rows * 8, 256)), dim3(256), 0, s, a, rows);
   else
-    hipLaunchKernelGGL(rowkey_kernel<bf16>, dim3(nblk(rows, 256)), dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL(rowkey_kernel<bf16>, dim3(nblk(rows * 8, 256)), dim3(256), 0, s, a, rows);
   return hipGetLastError();
 }
 
