@@ -81,10 +81,12 @@ def reduction_bytes(spec, delta):
     Each offset-gradient entry dZ~[i, s] in the band rows 1 .. 2D-1 that token
     i reaches is read once by each kernel that consumes it: the finalize
     kernel (dQ += dZ~ A~, only with a table on that side) and the partials
-    kernel (the table- and bias-gradient chunk sums); the fp32 dQ / dK
-    partial is read and the dQ / dK output (fp32 here) written.  Entries are
-    2 bytes (bf16, or fp16 for the Transformer-XL v term), 4 with a scalar
-    bias.  Table tiles, boundary sums and chunk partials are not counted."""
+    kernel (the table- and bias-gradient chunk sums); with a table term on
+    that side (A^Q; A^K or u) the fp32 dQ / dK partial is read and the dQ / dK
+    output (fp32 here) written, else the pass writes the output itself and
+    the stage moves no token bytes.  Entries are 2 bytes (bf16, or fp16 for
+    the Transformer-XL v term), 4 with a scalar bias.  Table tiles, boundary
+    sums and chunk partials are not counted."""
     import numpy as np
     B, H, N, D = spec["B"], spec["H"], spec["N"], delta
     causal, terms = spec["causal"], spec["terms"]
@@ -98,11 +100,13 @@ def reduction_bytes(spec, delta):
     q_entries = band(np.zeros(N, np.int64) if causal else i - (N - 1), i)
     k_entries = band(np.zeros(N, np.int64) if causal else -i, (N - 1) - i)
     tok = B * H * N * 64 * (4 + 4)
+    q_tok = tok if "aq" in terms else 0
+    k_tok = tok if ("ak" in terms or "u" in terms) else 0
     q_reads = ("aq" in terms) + any(t in terms for t in ("aq", "bias", "v"))
     q_size = 4 if "bias" in terms else 2
     k_reads = 2 if "ak" in terms else 0
-    return (tok + q_reads * B * H * q_entries * q_size,
-            tok + k_reads * B * H * k_entries * 2)
+    return (q_tok + q_reads * B * H * q_entries * q_size,
+            k_tok + k_reads * B * H * k_entries * 2)
 
 
 def measured_stage_traffic(stage):
@@ -334,8 +338,8 @@ def main():
                 for name, ms in (("attn_fwd", attn), ("bwd_q", kq), ("bwd_k", kk))},
             "reduce_ms": {"query": round(rq, 4), "key": round(rk, 4)},
             "reduce_bytes": {"query": r.red_bytes[0], "key": r.red_bytes[1]},
-            "reduce_gbps": {"query": round(r.red_bytes[0] / rq / 1e6, 1),
-                            "key": round(r.red_bytes[1] / rk / 1e6, 1)},
+            "reduce_gbps": {"query": round(r.red_bytes[0] / rq / 1e6, 1) if r.red_bytes[0] else None,
+                            "key": round(r.red_bytes[1] / rk / 1e6, 1) if r.red_bytes[1] else None},
         }
         if r.name in mem:
             d["fwd_peak_mib"] = round(mem[r.name][0], 1)

@@ -36,12 +36,14 @@ def test_reduction_bytes_brute_force(N, D, causal, terms):
     B, H = 2, 3
     spec = {"B": B, "H": H, "N": N, "causal": causal, "terms": terms}
     q, k = bench.reduction_bytes(spec, D)
-    tok = B * H * N * 64 * 8
+    tok = B * H * N * 64 * 8  # fp32 partial read + fp32 output written
+    q_tok = tok if "aq" in terms else 0
+    k_tok = tok if ("ak" in terms or "u" in terms) else 0
     q_reads = ("aq" in terms) + 1  # every term list here has a query-side entry
     q_size = 4 if "bias" in terms else 2
     k_reads = 2 if "ak" in terms else 0
-    assert q == tok + q_reads * B * H * _entries(N, D, causal, False) * q_size
-    assert k == tok + k_reads * B * H * _entries(N, D, causal, True) * 2
+    assert q == q_tok + q_reads * B * H * _entries(N, D, causal, False) * q_size
+    assert k == k_tok + k_reads * B * H * _entries(N, D, causal, True) * 2
 
 
 def test_causal_credit_counts_visible_pairs():
