@@ -30,6 +30,7 @@ template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int total, int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
+  constexpr bool HOISTQ = (F & F_ZQ) && (F & F_CAUSAL);
   constexpr bool DZ = (F & F_DZQ) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
@@ -280,13 +281,30 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
+        // causal identity maps (every tile a band tile): the block's four
+        // Z^Q runs are requested together, one memory round trip per block
+        // instead of four
+        uint2 zw[4];
+        if constexpr (HOISTQ) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int j1 = j0 + 16 * kb + 4 * g;
+            const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+            zw[kb] = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const int j1 = j0 + 16 * kb + 4 * g;
           float zq[4] = {0.f, 0.f, 0.f, 0.f};
           if (F & F_ZQ) {
-            const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
-            const uint2 w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            uint2 w;
+            if constexpr (HOISTQ) {
+              w = zw[kb];
+            } else {
+              const int c0 = clamp_run((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad, giq[qb].pitch);
+              w = bload8(rzq, iok ? static_cast<uint32_t>((zrow + c0) * 2) : kOob);
+            }
             const halfx4 hv = __builtin_bit_cast(halfx4, w);
 #pragma unroll
             for (int t = 0; t < 4; ++t) zq[t] = static_cast<float>(hv[3 - t]);
