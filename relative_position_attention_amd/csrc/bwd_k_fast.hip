@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   }
   GroupInfo gik = {0, 0, 0, 0};
   const int gk0 = (j0b / kGroup) * kGroup;  // (used without PAIR only)
-  if ((F & F_ZK) || DZ) gik = a.gk[j0b / kGroup];
+  if ((F & F_ZK) || DZ) gik = sload_uniform16(a.gk + j0b / kGroup);
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
     rzq = make_rsrc(reinterpret_cast<const _Float16*>(a.zq) + bh * a.zq_bh,

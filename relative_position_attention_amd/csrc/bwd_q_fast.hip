@@ -129,12 +129,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       gq0[qb] = (qbase[qb] / kGroup) * kGroup;
-      if (((F & F_ZQ) || DZ) && qon[qb]) giq[qb] = a.gq[qbase[qb] / kGroup];
+      if (((F & F_ZQ) || DZ) && qon[qb]) giq[qb] = sload_uniform16(a.gq + qbase[qb] / kGroup);
     }
   } else {
-    // both blocks in the workgroup's group
+    // both blocks in the workgroup's group (group records come through the
+    // scalar cache: they stay in scalar registers)
     gq0[0] = gq0[1] = i0;
-    if ((F & F_ZQ) || DZ) giq[0] = giq[1] = a.gq[i0 / kGroup];
+    if ((F & F_ZQ) || DZ) giq[0] = giq[1] = sload_uniform16(a.gq + i0 / kGroup);
   }
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
@@ -144,7 +145,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
-  GT* dzslice = DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh : nullptr;
+  // offset gradients through a buffer resource: 32-bit element offsets (no
+  // 64-bit row pointers to keep in registers) and range-checked stores
+  const Rsrc rdz = make_rsrc(DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh : nullptr,
+                             DZ ? static_cast<uint64_t>(a.dz_bh) * sizeof(GT) : 0);
 
   // key-tile ranges of each block: tiles [0, nkq) are visible; [0, n_hi) have
   // delta >= D for every pair of the block, [t_lo, nkq) delta <= -D
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       // band for some wave of the workgroup: stage Z^K of the tile's keys
       const bool blk_sat = (i0 - (j0 + 63) >= D) || (i0 + 127 - j0 <= -D);
       if (!blk_sat && j0 < N) {
-        const GroupInfo gk = a.gk[j0 / kGroup];
+        const GroupInfo gk = sload_uniform16(a.gk + j0 / kGroup);
         stage_zk_rows(rzk, gk.base, gk.slo, gk.pad, gk.pitch, (j0 / kGroup) * kGroup, j0, i0, D,
                       szk, kZP);
         __syncthreads();
@@ -277,6 +281,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         pure[qb] = qa - (j0 + 63) > -D && qz - j0 < D;
       }
       float off[2];
+      // transposing-read address of this lane in szk (lds_tr4 with row0 = 4g)
+      const _Float16* szk_lane = szk + (4 * g + (c16 >> 2)) * kZP + 4 * (c16 & 3);
       auto band_q = [&](int qb, auto PURE) {
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
@@ -316,9 +322,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
             khi4 = *reinterpret_cast<const floatx4*>(&skc[buf][1][16 * kb + 4 * g]);
           }
           halfx4 zk4 = halfx4{0, 0, 0, 0};
-          if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3
-            zk4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szk), kZP,
-                                                     16 * kb + 4 * g, qbase[qb] - i0, c16));
+          if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3 (the lane's base, plus rows 16 kb and the block's columns)
+            zk4 = __builtin_bit_cast(halfx4, lds_tr4_at(szk_lane + (16 * kb) * kZP + (qbase[qb] - i0)));
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int j = j1 + t;
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
             continue;
           }
           const int i = qbase[qb] + c16;
-          GT* rowp = dzslice + giq[qb].base + static_cast<int64_t>(i - gq0[qb]) * giq[qb].pitch;
+          const int rowe = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch - giq[qb].slo + giq[qb].pad;
           auto dz_band = [&](auto PURE) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -426,7 +431,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
                 }
                 run[3 - t] = bandv;  // descending columns
               }
-              if (any) store4(rowp + ((i - (j1 + 3) + D) - giq[qb].slo + giq[qb].pad), run);
+              // (issued whether or not the run holds a band pair: a run
+              // without one stores nothing)
+              bstore4(rdz, any ? static_cast<uint32_t>(rowe + (i - (j1 + 3) + D)) * sizeof(GT) : kOob, run,
+                      static_cast<GT*>(nullptr));
             }
           };
           if (pure[qb])

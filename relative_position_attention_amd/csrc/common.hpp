@@ -191,6 +191,14 @@ __device__ __forceinline__ bf16x4 lds_tr4(const bf16* tile, int pitch, int row0,
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// The same read at a lane address computed by the caller (lane r addresses
+// row r/4 of its group, columns 4 (r%4) .. +3, as above).
+__device__ __forceinline__ bf16x4 lds_tr4_at(const void* p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- fp16 operands.  fp16 and bf16 words are both 16-bit, so a tile keeps
@@ -294,6 +302,30 @@ __device__ __forceinline__ float bloadf(Rsrc r, uint32_t off) {
 }
 __device__ __forceinline__ _Float16 bloadh(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// Four values as a range-checked buffer store of the element type (offset in
+// bytes; kOob stores nothing).
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float* in, bf16*) {
+  bf16x4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = static_cast<bf16>(in[t]);
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float* in, _Float16*) {
+  halfx4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = static_cast<_Float16>(in[t]);
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(Rsrc r, uint32_t off, const float* in, float*) {
+  floatx4 v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = in[t];
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, 0);
 }
 
 // Output element store (O, dQ, dK, dV) in the output dtype.

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
     const int qg = qbase[PAIR ? qb : 0] / kGroup;
     gq0[qb] = qg * kGroup;
     giq[qb] = GroupInfo{0, 0, 0, 0};
-    if ((F & F_ZQ) && qon[qb]) giq[qb] = a.gq[qg];
+    if ((F & F_ZQ) && qon[qb]) giq[qb] = sload_uniform16(a.gq + qg);
   }
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
