@@ -27,7 +27,7 @@
 //   exact quotient.
 //   O^T += V^T P^T on MFMA with P in registers (bf16, or a bf16 hi + lo pair
 //   under F_SPLIT); the row sums of P are one more MFMA with a ones operand
-//   (fp32 vector sums under F_SPLIT).
+//   (two under F_SPLIT, one per part).
 // The region of each tile is decided per wave from the wave's extreme offsets
 // before the loop (the three ranges of [RPA] §4.3.3).
 #include "relation.hpp"
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
     const int qg = qbase[PAIR ? qb : 0] / kGroup;
     gq0[qb] = qg * kGroup;
     giq[qb] = GroupInfo{0, 0, 0, 0};
-    if ((F & F_ZQ) && qon[qb]) giq[qb] = sload_uniform16(a.gq + qg);
+    if ((F & F_ZQ) && qon[qb]) giq[qb] = a.gq[qg];
   }
   Rsrc rzq = rq, rzk = rq, rbt = rq;
   if (F & F_ZQ)
@@ -433,22 +433,16 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
           for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
         }
         const float bias = off[qb] - mu[qb];
-        float lv = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float p = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
-            s[qb][kb][t] = p;
-            if (SPLIT) lv += p;
-          }
-        if (SPLIT) l[qb] += wave_sum_g(lv);
+          for (int t = 0; t < 4; ++t) s[qb][kb][t] = fast_exp2(fmaf(s[qb][kb][t], sl2, bias));
       }
 
       // ---- O^T += V^T P^T (keys in the permuted order of frag_regs); the
       // row sums of P come from the same MFMA with a row of ones for V^T, so
-      // they add exactly the bf16 weights that multiply V (with split operands
-      // they are summed in fp32 above: the hi part alone would not match)
+      // they add exactly the bf16 weights that multiply V (with split
+      // operands both parts, hi and lo, go through the ones product)
       floatx4 ls[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) ls[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -483,19 +477,16 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void a
               o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[qb], o[qb][db], 0, 0, 0);
           }
         }
-        if (!SPLIT) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            if (qb == 0 && !act[0]) continue;
-            ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[qb], ls[qb], 0, 0, 0);
-          }
+        for (int qb = 0; qb < QB; ++qb) {
+          if (qb == 0 && !act[0]) continue;
+          ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pf[qb], ls[qb], 0, 0, 0);
+          if (SPLIT) ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pl[qb], ls[qb], 0, 0, 0);
         }
       }
-      if (!SPLIT) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          if (act[qb]) l[qb] += ls[qb][0];
-      }
+      for (int qb = 0; qb < QB; ++qb)
+        if (act[qb]) l[qb] += ls[qb][0];
     }
 
     // buffer buf ^ 1 was last read in iteration kt - 1, which every wave
