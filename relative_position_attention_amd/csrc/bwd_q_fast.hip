@@ -214,6 +214,13 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     const int j0 = kt * 64;
+    // With a key table the pass sits at the register limit: the lane index
+    // is made opaque each tile so the per-lane LDS addresses derived from it
+    // are recomputed in the tile (a few adds) instead of being kept across the
+    // loop, where they spilled to scratch and were reloaded every tile.
+    int lane_t = lane;
+    if constexpr (STZK) asm volatile("" : "+v"(lane_t));
+    const int g = lane_t >> 4, c16 = lane_t & 15;
     if (kt + 1 < nkt) load_tile(j0 + 64);
     if (STZK) {
       // band for some wave of the workgroup: stage Z^K of the tile's keys
