@@ -46,7 +46,7 @@ constexpr float kLazy = 8.f;       // rescale threshold, log2 units
 #define kOnes8 (__builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}))
 
 template <int F>
-__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL)) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
+__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U)) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
                                                           int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
