@@ -30,7 +30,7 @@ template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int total, int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
-  constexpr bool HOISTQ = (F & F_ZQ) && (F & F_CAUSAL);
+  constexpr bool HOISTQ = (F & F_ZQ) && !(F & F_ZK);
   constexpr bool DZ = (F & F_DZQ) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
@@ -294,9 +294,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
-        // causal identity maps (every tile a band tile): the block's four
-        // Z^Q runs are requested together, one memory round trip per block
-        // instead of four
+        // without a key table (room in the registers): the block's four Z^Q
+        // runs are requested together, one memory round trip per block
+        // instead of four (every tile of an identity map is a band tile)
         uint2 zw[4];
         if constexpr (HOISTQ) {
 #pragma unroll
