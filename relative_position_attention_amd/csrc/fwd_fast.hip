@@ -61,10 +61,11 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U)) ? 
   constexpr bool PAIR = CAUSAL && !STZK;
   constexpr int kZP = 136;  // szk pitch (fp16)
   // Z^Q runs of band tiles under causal masks (every tile of an identity map
-  // is a band tile): issued for all blocks at the top of the step, before the
+  // is a band tile) and with a key table (two waves per SIMD leave the
+  // registers): issued for all blocks at the top of the step, before the
   // next tile's prefetch, so that waiting for them leaves the prefetch in
   // flight.  Elsewhere band tiles are few and the runs are loaded where used.
-  constexpr bool HOIST = (F & F_ZQ) && CAUSAL;
+  constexpr bool HOIST = (F & F_ZQ) && (CAUSAL || (F & F_ZK));
   __shared__ __attribute__((aligned(16))) _Float16 szk[STZK ? 64 * kZP : 8];
   __shared__ __attribute__((aligned(16))) bf16 sk[2][64 * kKP];
   __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kKP];
@@ -245,7 +246,15 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U)) ? 
     // reads Z^Q[i][i - j1 - t + D], t = 0..3, i = qbase + c16,
     // j1 = j0 + 16 kb + 4g (a run in descending column order).
     uint2 zqr[QB][4];
-    if (HOIST) {
+    // (with a key table most tiles are saturated: the runs are requested
+    // only on tiles where some block is in the band, a uniform branch)
+    bool anyband = !STZK;
+    if (STZK) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        anyband = anyband || (kt < nkt_w && !(kt < n_hi[qb] || kt >= t_lo[qb]));
+    }
+    if (HOIST && anyband) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const bool bandq = kt < nkt_w && (PAIR ? kt < nkq[qb] : true) &&
