@@ -268,8 +268,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     // blocks (qb, kb) reads Z^K[j][i1 - j + D], i1 = i0 + 16 qb + 4g + t,
     // t = 0..3, j = jbase[kb] + c16 (an ascending run).
     uint2 zkr[2][2];
-    if (F & F_ZK) {
-      const bool bandk = it >= itw && !(it < n_lo[0] || it >= t_hi[0]);
+    // (requested on band tiles only, a uniform branch: most tiles of a key
+    // table's map are saturated, and out-of-range loads still cost)
+    const bool bandk = (F & F_ZK) && it >= itw && !(it < n_lo[0] || it >= t_hi[0]);
+    if (bandk) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
           const int i1 = i0 + 16 * qb + 4 * g;
           const int j = jbase[kb] + c16;
           const int c0 = clamp_run((i1 - j + D) - gik.slo + gik.pad, gik.pitch);
-          zkr[qb][kb] = bload8(rzk, (bandk && j < N)
+          zkr[qb][kb] = bload8(rzk, j < N
               ? static_cast<uint32_t>((gik.base + (j - gk0) * gik.pitch + c0) * 2) : kOob);
         }
     }
