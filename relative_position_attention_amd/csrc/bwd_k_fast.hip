@@ -212,8 +212,11 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     const bool sat0 = (i0 - (jr0 + 63) >= D) || (i0 + kT - 1 - jr0 <= -D);
     const bool sat1 = (i0 - (jr1 + 63) >= D) || (i0 + kT - 1 - jr1 <= -D);
     const bool need = t < nqt && !(sat0 && sat1);
-    GroupInfo gq = {0, 0, 0, 0};
-    if (need) gq = sload_uniform16(a.gq + i0 / kGroup);
+    // (a uniform branch: a tile saturated for both halves reads no Z^Q, and
+    // out-of-range loads still cost; its LDS copy is then never read)
+    zr[0] = zr[1] = uint4{0, 0, 0, 0};
+    if (!need) return;
+    const GroupInfo gq = sload_uniform16(a.gq + i0 / kGroup);
     const int gq0s = (i0 / kGroup) * kGroup;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       const int i = i0 + r;
       const int col = (i - jtop + D) - gq.slo + gq.pad + 8 * chl;
       const int e = gq.base + (i - gq0s) * gq.pitch + col;
-      zr[u] = bload16(rzq, (need && i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
+      zr[u] = bload16(rzq, (i < N && e >= 0) ? static_cast<uint32_t>(e) * 2 : kOob);
     }
   };
   auto store_zq = [&](int buf) {
