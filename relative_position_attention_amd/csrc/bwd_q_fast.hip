@@ -221,9 +221,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     int lane_t = lane;
     if constexpr (STZK) asm volatile("" : "+v"(lane_t));
     const int g = lane_t >> 4, c16 = lane_t & 15;
-    if (kt + 1 < nkt) load_tile(j0 + 64);
     if (STZK) {
       // band for some wave of the workgroup: stage Z^K of the tile's keys
+      // (before the next tile's prefetch is issued: loads complete in order,
+      // so the staging's wait would otherwise cover the prefetch too)
       const bool blk_sat = (i0 - (j0 + 63) >= D) || (i0 + 127 - j0 <= -D);
       if (!blk_sat && j0 < N) {
         const GroupInfo gk = sload_uniform16(a.gk + j0 / kGroup);
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         __syncthreads();
       }
     }
+    if (kt + 1 < nkt) load_tile(j0 + 64);
 
     if (kt < nkt_w) {
       const bf16* Ks = sk[buf];
