@@ -83,6 +83,23 @@ def test_saturated_tiles_small_delta():
     _case("shaw-D16-N1024", spec, arr)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_explicit_map(causal):
+    # an explicit row table ([RPA] relation map as a lookup over clipped
+    # offsets): monotone, so every row's offsets are contiguous, with runs of
+    # equal rows (bucket copies) and 11 rows for 17 offsets; N = 300 leaves a
+    # ragged tile
+    spec, arr = make_problem(kind="shaw", B=1, H=2, N=300, dtype="bf16", seed=7, clip=8,
+                             shared_table=False, causal=causal)
+    spec = copy.deepcopy(spec)
+    spec["map"] = {"kind": "explicit", "clip": 8,
+                   "rows": [0, 0, 0, 1, 1, 2, 3, 4, 5, 6, 7, 8, 8, 9, 10, 10, 10]}
+    spec["rows"] = 11
+    arr = dict(arr)
+    arr["aq"] = np.ascontiguousarray(arr["aq"][:11])
+    _case(f"explicit-causal{int(causal)}", spec, arr)
+
+
 def test_bf16_outputs_round_once():
     # bf16 output mode writes the fp32-mode O (and dV, which does not depend
     # on O) rounded once: within one bf16 unit in the last place.  (dQ and dK
