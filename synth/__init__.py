@@ -15,6 +15,7 @@ from .problems import (  # noqa: F401
     CONFIGS,
     BENCH_SHAPES,
     make_problem,
+    make_mixed,
     make_config,
     make_bench,
     round_to_dtype,

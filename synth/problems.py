@@ -134,6 +134,34 @@ def make_problem(kind, B, H, N, dtype, seed, *, causal=False, clip=16, qkv_std=1
     return spec, arrays
 
 
+def make_mixed(terms, B, H, N, dtype, seed, *, causal=False, clip=16, term_std=0.5):
+    """A problem with any subset of the relation terms over one clipped map
+    (row = clip(x, -clip, clip) + clip of the signed offset), for the term
+    combinations no single mechanism uses: per-head tables, bias, u and v all
+    N(0, term_std^2), so each term moves the scores visibly at tau = 1/8."""
+    d = D_HEAD
+    rng = np.random.default_rng(seed)
+    arrays = {name: _normal(rng, (B, H, N, d), 1.0) for name in ("q", "k", "v", "do")}
+    R = 2 * clip + 1
+    spec = {"name": "mixed-" + "+".join(terms), "B": B, "H": H, "N": N, "d": d,
+            "dtype": dtype, "causal": bool(causal), "signs": {"aq": 1, "ak": -1, "bias": 1},
+            "aq_shared": False, "scale": 1.0 / math.sqrt(d),
+            "map": {"kind": "clipped", "clip": clip}, "terms": list(terms), "rows": R}
+    if "aq" in terms:
+        arrays["aq"] = _normal(rng, (R, H, d), term_std)
+    if "ak" in terms:
+        arrays["ak"] = _normal(rng, (R, H, d), term_std)
+    if "bias" in terms:
+        arrays["bias"] = _normal(rng, (R, H), term_std)
+    if "u" in terms:
+        arrays["u"] = _normal(rng, (H, d), term_std)
+    if "v" in terms:
+        arrays["v_bias"] = _normal(rng, (H, d), term_std)
+    for key in list(arrays):
+        arrays[key] = round_to_dtype(arrays[key], dtype)
+    return spec, arrays
+
+
 # The five parity configurations (seed = configuration number).
 CONFIGS = {
     1: dict(kind="shaw", B=1, H=2, N=128, dtype="f32", seed=1, clip=16,

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from synth import make_problem, scaled_config
+from synth import make_mixed, make_problem, scaled_config
 from gpu_util import check, run_library
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +98,25 @@ def test_explicit_map(causal):
     arr = dict(arr)
     arr["aq"] = np.ascontiguousarray(arr["aq"][:11])
     _case(f"explicit-causal{int(causal)}", spec, arr)
+
+
+_COMBOS = [["ak"], ["aq", "bias"], ["ak", "bias"], ["aq", "ak", "bias"], ["bias", "u"],
+           ["aq", "u"], ["aq", "v"], ["aq", "ak", "bias", "u", "v"]]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("terms", _COMBOS, ids=["+".join(c) for c in _COMBOS])
+def test_term_combinations(terms, causal):
+    # term sets that no single mechanism uses, over one clipped map, in fp32
+    # (tolerance 1e-4): every query-side and key-side flag combination of the
+    # passes, N = 200 leaving ragged tiles
+    spec, arr = make_mixed(terms, 1, 2, 200, "f32", 11, causal=causal)
+    _case(f"{spec['name']}-causal{int(causal)}", spec, arr)
+
+
+def test_all_terms_bf16():
+    spec, arr = make_mixed(["aq", "ak", "bias", "u", "v"], 2, 3, 333, "bf16", 12, causal=False)
+    _case(spec["name"] + "-bf16", spec, arr)
 
 
 def test_bf16_outputs_round_once():
