@@ -119,6 +119,28 @@ def test_all_terms_bf16():
     _case(spec["name"] + "-bf16", spec, arr)
 
 
+def test_t5_unidirectional_causal():
+    # decoder-style T5 buckets (no separate half for keys after the query),
+    # causal, with the recipe's split operands
+    spec, arr = make_problem(kind="t5", B=1, H=2, N=300, dtype="bf16", seed=21, causal=True)
+    spec = copy.deepcopy(spec)
+    spec["map"]["bidirectional"] = False
+    _case("t5-unidirectional-causal", spec, arr)
+
+
+def test_deberta_small_buckets():
+    # log buckets with bucket size 32 and maximum position 128: a band of 257
+    # offsets over 64 table rows, so N = 300 has saturated tiles on both sides
+    spec, arr = make_problem(kind="deberta", B=1, H=2, N=300, dtype="bf16", seed=22)
+    spec = copy.deepcopy(spec)
+    spec["map"] = {"kind": "log", "bucket_size": 32, "max_position": 128}
+    spec["rows"] = 64
+    arr = dict(arr)
+    arr["aq"] = np.ascontiguousarray(arr["aq"][:64])
+    arr["ak"] = np.ascontiguousarray(arr["ak"][:64])
+    _case("deberta-b32-p128", spec, arr)
+
+
 def test_bf16_outputs_round_once():
     # bf16 output mode writes the fp32-mode O (and dV, which does not depend
     # on O) rounded once: within one bf16 unit in the last place.  (dQ and dK
