@@ -76,6 +76,21 @@ def test_small_and_ragged(N, dtype):
             _case(f"{kind}-{dtype}-N{N}-c{int(causal)}", spec, arr)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["shaw", "t5", "deberta", "txl"])
+def test_f32_several_groups(kind, causal):
+    # fp32 inputs (tolerance 1e-4) over five 128-query groups and a ragged
+    # tail, with bands narrower than the sequence (clip 40; DeBERTa's default
+    # buckets; the identity map of Transformer-XL).  T5 runs with tau = 1/8:
+    # at its own tau = 1 the scores of unit-variance inputs make |dQ| reach
+    # ~30, where fp32 rounding alone is ~1e-4 absolute (rel-L2 2e-6)
+    spec, arr = make_problem(kind=kind, B=2, H=2, N=600, dtype="f32", seed=31, causal=causal,
+                             clip=40, d_model=128)
+    if kind == "t5":
+        spec = dict(spec, scale=0.125)
+    _case(f"{kind}-f32-N600-c{int(causal)}", spec, arr)
+
+
 def test_saturated_tiles_small_delta():
     # N = 1024 with delta 16: most tiles saturated on both sides
     spec, arr = make_problem(kind="shaw", B=1, H=2, N=1024, dtype="bf16", seed=5, clip=16,
