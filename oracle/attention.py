@@ -28,7 +28,7 @@ by all heads).  Everything is float64.
 
 import numpy as np
 
-from .maps import map_rows, relation_rows
+from .maps import relation_rows
 
 
 def _has(spec, term):
@@ -206,40 +206,3 @@ def backward(spec, arrays):
     res = forward_backward(spec, arrays)
     return {key: val for key, val in res.items() if key not in ("o", "lse")}
 
-
-def query_rows_forward(spec, arrays, b, h, rows_idx):
-    """O and L for selected query rows only, at O(len(rows_idx) * N * d) cost.
-
-    Used to check outputs at sizes where the full N x N matrix is too large to
-    revisit for every slice.  Same definition as ``slice_forward``.
-    """
-    N = spec["N"]
-    tau = float(spec["scale"])
-    ii = np.asarray(rows_idx, dtype=np.int64)
-    q = arrays["q"][b, h][ii]
-    k = arrays["k"][b, h]
-    jj = np.arange(N, dtype=np.int64)
-    delta = ii[:, None] - jj[None, :]
-    if spec["causal"]:
-        delta = np.maximum(delta, 0)  # masked pairs: any valid row, never used
-    s = (q + arrays["u"][h] if _has(spec, "u") else q) @ k.T
-    if _has(spec, "aq"):
-        a = _aq(spec, arrays, h)
-        qp = q + arrays["v_bias"][h] if _has(spec, "v") else q
-        rq = map_rows(spec["map"], spec["signs"]["aq"] * delta)
-        s += np.einsum("nd,njd->nj", qp, a[rq])
-    if _has(spec, "ak"):
-        a = arrays["ak"][:, h, :]
-        rk = map_rows(spec["map"], spec["signs"]["ak"] * delta)
-        s += np.einsum("jd,njd->nj", k, a[rk])
-    if _has(spec, "bias"):
-        rb = map_rows(spec["map"], spec["signs"]["bias"] * delta)
-        s += arrays["bias"][:, h][rb]
-    s *= tau
-    if spec["causal"]:
-        s[jj[None, :] > ii[:, None]] = -np.inf
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    ssum = e.sum(axis=1, keepdims=True)
-    o = (e / ssum) @ arrays["v"][b, h]
-    return o, (m + np.log(ssum))[:, 0]
