@@ -101,7 +101,10 @@ typedef struct relpos_desc {
      significant bits, [RPA] "Half-precision numerics"); 1 = a bf16 pair
      hi + lo (about 16 significant bits; one more MFMA product each), for a
      strongly peaked softmax such as tau = 1 with unit-variance inputs, where
-     an 8-bit P moves O, hence D = rowdot(dO, O), by more than 2^-9. */
+     an 8-bit P moves O, hence D = rowdot(dO, O), by more than 2^-9.
+     The T5 mechanism at tau = 1 (bias as the only term, no 1/sqrt(d)) with
+     unit-variance inputs needs 1 to stay within max-abs 2e-2 on O and every
+     gradient; Shaw, DeBERTa and Transformer-XL meet it with 0. */
   int32_t split_operands;
   relpos_map map;
   /* Table layouts, in elements.  A^Q, A^K: element (r, h, e) at

@@ -169,3 +169,22 @@ def test_stage_events_validation():
     assert lib.relpos_set_stage_events(arr, 9) == -1
     assert lib.relpos_set_stage_events(None, 2) == -1
     assert lib.relpos_set_stage_events(arr, 0) == 0
+
+
+def test_t5_descriptors_take_split_operands():
+    # the T5 configuration (tau = 1, unit-variance inputs) meets the bf16
+    # tolerances only with split operands; the parity harness and the bench
+    # must build its descriptor that way, and the others with single operands
+    import bench
+    from gpu_util import split_operands_for
+    spec2 = make_problem(**dict(CONFIGS[2], N=64))[0]
+    assert "split_operands" not in spec2  # not an input-recipe property
+    assert rpa.Problem(spec2, split_operands=split_operands_for(spec2)).desc.split_operands == 1
+    for name in BENCH_SHAPES:
+        spec = make_problem(**dict(BENCH_SHAPES[name], N=64))[0]
+        want = 1 if name == "t5" else 0
+        assert bench.bench_problem(rpa, name, spec, "f32").desc.split_operands == want, name
+        assert int(split_operands_for(spec)) == want, name
+    for idx in (1, 3, 4, 5):
+        spec = make_problem(**dict(CONFIGS[idx], N=64))[0]
+        assert not split_operands_for(spec), idx

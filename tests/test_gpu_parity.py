@@ -136,7 +136,7 @@ def test_all_terms_bf16():
 
 def test_t5_unidirectional_causal():
     # decoder-style T5 buckets (no separate half for keys after the query),
-    # causal, with the recipe's split operands
+    # causal, with the split operands of the T5 score form
     spec, arr = make_problem(kind="t5", B=1, H=2, N=300, dtype="bf16", seed=21, causal=True)
     spec = copy.deepcopy(spec)
     spec["map"]["bidirectional"] = False
