@@ -50,14 +50,49 @@ struct PlanCache {
 thread_local PlanCache g_plans;
 constexpr size_t kPlanCacheSize = 16;
 
+// The key is built field by field, so padding bytes of the caller's structs
+// (uninitialised in C) never enter it.
+template <typename T>
+void put(std::string& key, T v) {
+  key.append(reinterpret_cast<const char*>(&v), sizeof v);
+}
+
 std::string plan_key(const relpos_desc* d, const relpos_shape* sh) {
-  std::string key(reinterpret_cast<const char*>(sh), sizeof(relpos_shape));
-  relpos_desc copy = *d;
-  copy.map.explicit_rows = nullptr;
-  key.append(reinterpret_cast<const char*>(&copy), sizeof copy);
-  if (d->map.kind == RELPOS_MAP_EXPLICIT && d->map.explicit_rows != nullptr && d->map.clip >= 0)
-    key.append(reinterpret_cast<const char*>(d->map.explicit_rows),
-               sizeof(int32_t) * (2 * static_cast<size_t>(d->map.clip) + 1));
+  std::string key;
+  key.reserve(160);
+  put(key, sh->B);
+  put(key, sh->H);
+  put(key, sh->N);
+  put(key, sh->d);
+  put(key, d->abi_version);
+  put(key, d->terms);
+  put(key, d->causal);
+  put(key, d->scale);
+  put(key, d->dtype);
+  put(key, d->out_dtype);
+  put(key, d->num_rows);
+  put(key, d->sign_q);
+  put(key, d->sign_k);
+  put(key, d->sign_b);
+  put(key, d->split_operands);
+  const relpos_map& m = d->map;
+  put(key, m.kind);
+  put(key, m.clip);
+  put(key, m.identity_offset);
+  put(key, m.num_buckets);
+  put(key, m.max_distance);
+  put(key, m.bidirectional);
+  put(key, m.bucket_size);
+  put(key, m.max_position);
+  put(key, d->aq_row_stride);
+  put(key, d->aq_head_stride);
+  put(key, d->ak_row_stride);
+  put(key, d->ak_head_stride);
+  put(key, d->bias_row_stride);
+  put(key, d->bias_head_stride);
+  if (m.kind == RELPOS_MAP_EXPLICIT && m.explicit_rows != nullptr && m.clip >= 0)
+    key.append(reinterpret_cast<const char*>(m.explicit_rows),
+               sizeof(int32_t) * (2 * static_cast<size_t>(m.clip) + 1));
   return key;
 }
 

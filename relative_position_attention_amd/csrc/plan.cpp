@@ -216,7 +216,7 @@ bool build_side(Plan& p, bool query_side, std::string& detail) {
     L.groups[g] = gi;
     base += static_cast<int64_t>(rows) * pitch;
     base = (base + 7) & ~static_cast<int64_t>(7);
-    if (base >= (static_cast<int64_t>(1) << 31) - 64) {
+    if (base >= (static_cast<int64_t>(1) << 31) - 64) {  // group bases are int32
       detail = "projection slice exceeds 2^31 elements (N too large for this map)";
       return false;
     }
@@ -224,6 +224,12 @@ bool build_side(Plan& p, bool query_side, std::string& detail) {
   L.bh_elems = base + 8;
   return true;
 }
+
+// The kernels address one (batch, head) slice of Z and of the offset
+// gradients through a buffer resource: 32-bit byte offsets, a range of at
+// most 2^31 - 1 bytes, and offset 2^31 as "no access".  A slice must
+// therefore stay below 2^31 bytes at its widest entry.
+constexpr int64_t kSliceByteLimit = (static_cast<int64_t>(1) << 31) - 256;
 
 }  // namespace
 
@@ -408,6 +414,26 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.need_qside = p.aq || p.bias || p.v;
   if (p.need_qside && !build_side(p, true, detail)) return RELPOS_E_UNSUPPORTED;
   if (p.ak && !build_side(p, false, detail)) return RELPOS_E_UNSUPPORTED;
+  // per-slice bytes at the entry widths: Z (z_size) on either side, and the
+  // one offset-gradient buffer (the larger side's elements at the wider
+  // entry) that both passes share
+  p.dz_entry = p.dzq_f32 ? 4 : (p.dzq_f16 ? 2 : p.g_size);
+  {
+    const int64_t zq = p.need_qside ? p.zq.bh_elems : 0, zk = p.ak ? p.zk.bh_elems : 0;
+    const int64_t zmax = std::max(zq, zk);
+    const int64_t zbytes = zmax * static_cast<int64_t>(p.z_size);
+    const int64_t gbytes = zmax * static_cast<int64_t>(p.dz_entry);
+    if (zbytes > kSliceByteLimit || gbytes > kSliceByteLimit) {
+      char buf[200];
+      std::snprintf(buf, sizeof buf,
+                    "a (batch, head) slice of the projections or offset gradients needs %lld "
+                    "bytes; the kernels address at most 2^31 - 256 per slice (N too large for "
+                    "this map)",
+                    static_cast<long long>(std::max(zbytes, gbytes)));
+      detail = buf;
+      return RELPOS_E_UNSUPPORTED;
+    }
+  }
 
   // Token chunks for the two-phase table-gradient sums ([RPA] "Deterministic
   // table gradients"): enough blocks to fill the chip.
@@ -481,9 +507,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   int64_t dz_elems = 0;
   if (p.need_qside) dz_elems = std::max(dz_elems, p.zq.bh_elems);
   if (p.ak) dz_elems = std::max(dz_elems, p.zk.bh_elems);
-  const size_t dz_entry = p.dzq_f32 ? 4 : (p.dzq_f16 ? 2 : p.g_size);
   p.ws_dz = off;
-  off = align256(off + static_cast<size_t>(p.BH) * dz_elems * dz_entry);
+  off = align256(off + static_cast<size_t>(p.BH) * dz_elems * p.dz_entry);
   p.ws_bndq = off;
   off = align256(off + 2 * bhn4);
   p.ws_bndk = off;

@@ -45,6 +45,7 @@ struct Plan {
   size_t t_size = 2, z_size = 2, g_size = 2;
   bool dzq_f32 = false;    // query-side offset gradients in fp32 (a scalar bias)
   bool dzq_f16 = false;    // query-side offset gradients in fp16 (v without a bias)
+  size_t dz_entry = 2;     // bytes per entry of the shared offset-gradient buffer
   bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
 

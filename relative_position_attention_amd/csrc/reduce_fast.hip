@@ -68,7 +68,7 @@ struct DzTile {
       const int ch = tq + 4 * u;
       const int ce = cf + ch * VEC;
       const bool ok = ch < NCH && ce >= 0 && ce <= e0 + 64 * W - 1 && hi >= 0 && lo <= 64 * W - 1 && lo <= hi;
-      w[u] = bload16(rz, ok ? static_cast<uint32_t>(ce) * sizeof(GT) : kOob);
+      w[u] = bload16(rz, ok ? static_cast<uint32_t>(ce * static_cast<int>(sizeof(GT))) : kOob);
     }
   }
 
