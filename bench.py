@@ -6,6 +6,12 @@ Transformer-XL causal) at its 8192-token shape: relpos_project +
 relpos_attn_fwd (the forward) and relpos_attn_bwd (the backward, retained
 projections), inputs resident in HBM.  Prints one JSON line.
 
+Timing follows the pages' appendix "Kernel benchmarks": a 512 MiB device
+write flushes the caches before every forward and every backward sample;
+each pass and kernel is reported as the median (with min and max) of the
+timed steps, measured with HIP events on the launch stream; GPU clocks,
+power and temperature are recorded (amd-smi) before and after.
+
 Useful FLOPs follow the credit of "Fast and Exact Relative-Position Attention
 via Structure-Aware Kernels" (§5.1 evaluation setup, throughput paragraph):
 forward 4 B H N^2 d + 2 B H N R d per projected table (none for T5), backward
@@ -184,24 +190,80 @@ class MechRun:
                      grads=self.grads, ws=self.ws_b)
 
 
-def peak_memory(run, torch, rpa):
+def peak_memory(run, torch, rpa, out_dtype):
     """Peak device MiB beyond the inputs of a forward and of a backward that
-    allocate their own buffers (the library itself never allocates)."""
+    allocate their own buffers, with O, dQ, dK, dV in `out_dtype` (the
+    library itself never allocates; [RPA] §5.2 "Memory footprint" counts the
+    device memory allocated beyond the inputs)."""
+    prob = bench_problem(rpa, run.name, run.spec, out_dtype)
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    o, lse, z = rpa.attn_fwd(run.prob, run.t, retain=True)
+    o, lse, z = rpa.attn_fwd(prob, run.t, retain=True)
     torch.cuda.synchronize()
     fwd = (torch.cuda.max_memory_allocated() - base) / 2**20
     base2 = torch.cuda.memory_allocated()  # inputs + O + L + retained z
     base2 -= z.numel()  # the retained projections count against the backward
     torch.cuda.reset_peak_memory_stats()
-    g = rpa.attn_bwd(run.prob, run.t, o, lse, run.t["do"], z=z)
+    g = rpa.attn_bwd(prob, run.t, o, lse, run.t["do"], z=z)
     torch.cuda.synchronize()
     bwd = (torch.cuda.max_memory_allocated() - base2) / 2**20
     del o, lse, z, g
     torch.cuda.empty_cache()
     return fwd, bwd
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def gpu_state():
+    """Clocks, power and temperature of GPU 0 as amd-smi reports them (the
+    pages record these instead of locking clocks): the numeric fields whose
+    names mention a clock, power or temperature, or the tool's error."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "-p", "-c", "-t", "--json"],
+                ["rocm-smi", "--showtemp", "--showpower", "--showclocks", "--json"]):
+        try:
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            err = str(e)
+            continue
+        if res.returncode != 0:
+            err = (res.stderr or res.stdout).strip()[-200:]
+            continue
+        try:
+            data = json.loads(res.stdout)
+        except ValueError:
+            err = res.stdout.strip()[-200:]
+            continue
+        out = {}
+
+        def walk(x, path):
+            if len(out) >= 40:
+                return
+            if isinstance(x, dict):
+                for k, v in x.items():
+                    walk(v, path + [str(k)])
+            elif isinstance(x, list):
+                for k, v in enumerate(x):
+                    walk(v, path + [str(k)])
+            else:
+                name = "/".join(path)
+                low = name.lower()
+                if any(t in low for t in ("clk", "clock", "power", "temp", "sclk", "mclk")):
+                    out[name] = x
+        walk(data, [])
+        return {"tool": cmd[0], "fields": out}
+    return {"tool": None, "error": err}
 
 
 def cpu_baseline(mechs):
@@ -232,7 +294,7 @@ def cpu_baseline(mechs):
             total_flops += f + b
         rounds += 1
     return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{rounds} x one (batch, head) slice of each of {','.join(mechs)} at N=8192, "
                       f"fp64 forward+backward ({total_s:.1f} s)"}
 
@@ -268,17 +330,20 @@ def main():
     mem = {}
     if not args.no_memory:
         for r in runs:
-            mem[r.name] = peak_memory(r, torch, rpa)
+            mem[r.name] = {od: peak_memory(r, torch, rpa, od) for od in ("f32", "bf16")}
 
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
-        return e
+    # Cache flush before every timed forward and backward sample ([RPA]
+    # appendix "Kernel benchmarks": an L2 flush before each sample): a write
+    # over 512 MiB, twice the 256 MB last-level cache, so that no pass finds
+    # its inputs or the projections left in cache by the one before
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=runs[0].t["q"].device)
 
     for _ in range(args.warmup):
         for r in runs:
+            flush.fill_(0.0)
             r.project(rpa)
             r.attn(rpa)
+            flush.fill_(0.0)
             r.backward(rpa)
     torch.cuda.synchronize()
 
@@ -293,95 +358,123 @@ def main():
         for pe, fe, be in row:
             for e in pe + fe + be:
                 e.record(stream)
+    state_before = gpu_state()
     torch.cuda.synchronize()
-    t_start = ev()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
     for step in range(args.steps):
         for k, r in enumerate(runs):
             pe, fe, be = marks[step][k]
+            flush.fill_(float(step))
             pe[0].record(stream)
             r.project(rpa)
             pe[1].record(stream)
             rpa.set_stage_events(fe)
             r.attn(rpa)
+            rpa.set_stage_events([])
+            flush.fill_(float(step))
             rpa.set_stage_events(be)
             r.backward(rpa)
             rpa.set_stage_events([])
-    t_end = ev()
+    t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    state_after = gpu_state()
+    wall_ms = t_start.elapsed_time(t_end) / args.steps
 
-    def avg(fn):
-        return sum(fn(m) for m in marks) / args.steps
+    def stats(fn):
+        """Median, min and max over the timed steps."""
+        xs = sorted(fn(m) for m in marks)
+        n = len(xs)
+        med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+        return med, xs[0], xs[-1]
+
+    # time of each step's passes (the flushes between them excluded)
+    step_ms = [sum(m[k][0][0].elapsed_time(m[k][1][1]) + m[k][2][0].elapsed_time(m[k][2][5])
+                   for k in range(len(runs))) for m in marks]
+    ms_per_step = sum(step_ms) / len(step_ms)
+
+    def r4(x):
+        return round(x, 4)
 
     per = {}
-    kernels = []  # (ms, mechanism, kernel)
-    reductions = []  # (ms, mechanism, stage, bytes)
+    kernels = []  # (median ms, mechanism, kernel)
+    reductions = []  # (median ms, mechanism, stage, bytes)
     step_flops = 0.0
     for k, r in enumerate(runs):
-        proj = avg(lambda m: m[k][0][0].elapsed_time(m[k][0][1]))
-        fwd = avg(lambda m: m[k][0][0].elapsed_time(m[k][1][1]))
-        attn = avg(lambda m: m[k][1][0].elapsed_time(m[k][1][1]))
-        bwd = avg(lambda m: m[k][2][0].elapsed_time(m[k][2][5]))
-        kq = avg(lambda m: m[k][2][1].elapsed_time(m[k][2][2]))
-        kk = avg(lambda m: m[k][2][3].elapsed_time(m[k][2][4]))
-        rq = avg(lambda m: m[k][2][2].elapsed_time(m[k][2][3]))
-        rk = avg(lambda m: m[k][2][4].elapsed_time(m[k][2][5]))
-        kernels += [(attn, r, "attn_fwd"), (kq, r, "bwd_q"), (kk, r, "bwd_k")]
-        reductions += [(rq, r, "query reduction", r.red_bytes[0]),
-                       (rk, r, "key reduction", r.red_bytes[1])]
+        proj = stats(lambda m: m[k][0][0].elapsed_time(m[k][0][1]))
+        fwd = stats(lambda m: m[k][0][0].elapsed_time(m[k][1][1]))
+        attn = stats(lambda m: m[k][1][0].elapsed_time(m[k][1][1]))
+        bwd = stats(lambda m: m[k][2][0].elapsed_time(m[k][2][5]))
+        kq = stats(lambda m: m[k][2][1].elapsed_time(m[k][2][2]))
+        kk = stats(lambda m: m[k][2][3].elapsed_time(m[k][2][4]))
+        rq = stats(lambda m: m[k][2][2].elapsed_time(m[k][2][3]))
+        rk = stats(lambda m: m[k][2][4].elapsed_time(m[k][2][5]))
+        kernels += [(attn[0], r, "attn_fwd"), (kq[0], r, "bwd_q"), (kk[0], r, "bwd_k")]
+        reductions += [(rq[0], r, "query reduction", r.red_bytes[0]),
+                       (rk[0], r, "key reduction", r.red_bytes[1])]
         step_flops += r.fwd_flops + r.bwd_flops
         d = {
             "shape": {x: r.spec[x] for x in ("B", "H", "N", "causal")},
-            "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
-            "project_ms": round(proj, 4), "attn_kernel_ms": round(attn, 4),
-            "fwd_tflops": round(r.fwd_flops / fwd / 1e9, 2),
-            "bwd_tflops": round(r.bwd_flops / bwd / 1e9, 2),
-            "fwd_pct_peak": round(100 * r.fwd_flops / fwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
-            "bwd_pct_peak": round(100 * r.bwd_flops / bwd / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
-            "kernel_ms": {"attn_fwd": round(attn, 4), "bwd_q": round(kq, 4),
-                          "bwd_k": round(kk, 4)},
+            "fwd_ms": r4(fwd[0]), "bwd_ms": r4(bwd[0]),
+            "fwd_ms_min_max": [r4(fwd[1]), r4(fwd[2])],
+            "bwd_ms_min_max": [r4(bwd[1]), r4(bwd[2])],
+            "project_ms": r4(proj[0]), "attn_kernel_ms": r4(attn[0]),
+            "fwd_tflops": round(r.fwd_flops / fwd[0] / 1e9, 2),
+            "bwd_tflops": round(r.bwd_flops / bwd[0] / 1e9, 2),
+            "fwd_pct_peak": round(100 * r.fwd_flops / fwd[0] / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
+            "bwd_pct_peak": round(100 * r.bwd_flops / bwd[0] / 1e9 / MI355X_BF16_DENSE_TFLOPS, 2),
+            "kernel_ms": {"attn_fwd": r4(attn[0]), "bwd_q": r4(kq[0]), "bwd_k": r4(kk[0])},
+            "kernel_ms_min_max": {"attn_fwd": [r4(attn[1]), r4(attn[2])],
+                                  "bwd_q": [r4(kq[1]), r4(kq[2])],
+                                  "bwd_k": [r4(kk[1]), r4(kk[2])]},
             "kernel_mfma_tflops": {
-                name: round(KERNEL_PRODUCTS[name] * r.pair_flops / ms / 1e9, 2)
+                name: round(KERNEL_PRODUCTS[name] * r.pair_flops / ms[0] / 1e9, 2)
                 for name, ms in (("attn_fwd", attn), ("bwd_q", kq), ("bwd_k", kk))},
-            "reduce_ms": {"query": round(rq, 4), "key": round(rk, 4)},
+            "reduce_ms": {"query": r4(rq[0]), "key": r4(rk[0])},
             "reduce_bytes": {"query": r.red_bytes[0], "key": r.red_bytes[1]},
-            "reduce_gbps": {"query": round(r.red_bytes[0] / rq / 1e6, 1) if r.red_bytes[0] else None,
-                            "key": round(r.red_bytes[1] / rk / 1e6, 1) if r.red_bytes[1] else None},
+            "reduce_gbps": {"query": round(r.red_bytes[0] / rq[0] / 1e6, 1) if r.red_bytes[0] else None,
+                            "key": round(r.red_bytes[1] / rk[0] / 1e6, 1) if r.red_bytes[1] else None},
         }
         if r.name in mem:
-            d["fwd_peak_mib"] = round(mem[r.name][0], 1)
-            d["bwd_peak_mib"] = round(mem[r.name][1], 1)
+            d["fwd_peak_mib"] = round(mem[r.name]["f32"][0], 1)
+            d["bwd_peak_mib"] = round(mem[r.name]["f32"][1], 1)
+            d["fwd_peak_mib_bf16_out"] = round(mem[r.name]["bf16"][0], 1)
+            d["bwd_peak_mib_bf16_out"] = round(mem[r.name]["bf16"][1], 1)
         per[r.name] = d
 
     # Dominant kernel: the single attention kernel (forward, query pass or key
-    # pass) with the longest average launch, timed live with the library's
+    # pass) with the longest median launch, timed live with the library's
     # stage events on the launch stream; its algorithmic MFMA FLOPs per launch
     # over that duration.
     dom_ms, dom, dom_kernel = max(kernels, key=lambda x: x[0])
     achieved = KERNEL_PRODUCTS[dom_kernel] * dom.pair_flops / dom_ms / 1e9
     roofline = {"bound": "mfma", "kernel": f"{dom_kernel} ({dom.name})",
-                "avg_launch_ms": round(dom_ms, 4),
+                "median_launch_ms": round(dom_ms, 4),
                 "flops_per_launch": KERNEL_PRODUCTS[dom_kernel] * dom.pair_flops,
                 "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
                 "traffic": measured_traffic(dom_kernel, dom.name)}
     if roofline["traffic"] is not None:
-        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, copy-calibrated)"
+        roofline["traffic_unit"] = ("bytes per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, "
+                                    "copy-calibrated; from the profiles/traffic_*.json summary "
+                                    "taken on the current kernel source)")
         roofline["traffic_tb_per_s"] = round(roofline["traffic"] / dom_ms / 1e9, 3)
 
     # HBM-bound stages: the offset-gradient reductions that produce the
     # table and bias gradients (dR / dBias), timed live with the stage events
-    # around them; the slowest one against the HBM peak
+    # around them (median over the steps); the slowest one against the HBM peak
     red_ms, red_run, red_stage, red_b = max(reductions, key=lambda x: x[0])
     hbm = {"bound": "hbm", "stage": f"{red_stage} ({red_run.name})",
            "kernels": "finalize + partials + fold (+ bias / v / u sums)",
-           "avg_ms": round(red_ms, 4), "bytes_per_call": red_b,
+           "median_ms": round(red_ms, 4), "bytes_per_call": red_b,
            "achieved": round(red_b / red_ms / 1e6, 1), "peak": MI355X_HBM_GBPS,
            "unit": "GB/s", "frac": round(red_b / red_ms / 1e6 / MI355X_HBM_GBPS, 4),
            "traffic": measured_stage_traffic(f"{red_stage} ({red_run.name})")}
     if hbm["traffic"] is not None:
-        hbm["traffic_unit"] = "bytes per call (rocprofv3 FETCH_SIZE, WRITE_SIZE, copy-calibrated)"
+        hbm["traffic_unit"] = ("bytes per call (rocprofv3 FETCH_SIZE, WRITE_SIZE, copy-calibrated; "
+                               "from profiles/traffic_reductions_n8192.json, taken on the current "
+                               "reduction sources)")
         hbm["traffic_gbps"] = round(hbm["traffic"] / red_ms / 1e6, 1)
 
     value = step_flops / ms_per_step / 1e9
@@ -401,6 +494,12 @@ def main():
         "config": {"workload": "relpos attention fwd+bwd at N=8192: " + ", ".join(
             f"{r.name} B{r.spec['B']} H{r.spec['H']}{' causal' if r.spec['causal'] else ''}"
             for r in runs), "mechanisms": mechs, "d": 64},
+        "timing": {"per_pass": "median (min, max) over the timed steps, HIP events on the "
+                               "launch stream", "flush": "512 MiB device write before every "
+                               "forward and every backward sample",
+                   "ms_per_step": "mean over the steps of the passes' own time (flushes "
+                                  "excluded)", "wall_ms_per_step_with_flushes": round(wall_ms, 4)},
+        "gpu_state": {"before": state_before, "after": state_after},
         "mechanisms": per,
         "roofline": roofline,
         "hbm": hbm,

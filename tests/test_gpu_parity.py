@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from synth import make_mixed, make_problem, scaled_config
-from gpu_util import check, run_library
+from gpu_util import check, errors, run_library
 
 pytestmark = pytest.mark.gpu
 
@@ -156,16 +156,51 @@ def test_deberta_small_buckets():
     _case("deberta-b32-p128", spec, arr)
 
 
-def test_bf16_outputs_round_once():
-    # bf16 output mode writes the fp32-mode O (and dV, which does not depend
-    # on O) rounded once: within one bf16 unit in the last place.  (dQ and dK
-    # are not compared: their D = rowdot(dO, O) takes the rounded O as input.)
-    spec, arr = scaled_config(2, B=1, H=2, N=256)
-    f32 = run_library(spec, arr, out_dtype="f32")
-    b16 = run_library(spec, arr, out_dtype="bf16")
-    for key in ("o", "dv"):
-        ulp = np.exp2(np.floor(np.log2(np.abs(f32[key]) + 1e-38)) - 7)
-        assert np.all(np.abs(b16[key] - f32[key]) <= ulp), key
+@pytest.mark.parametrize("idx,N", [(3, 700), (4, 500), (5, 400)])
+def test_bf16_outputs_against_oracle(idx, N):
+    # bf16 output mode (O, dQ, dK, dV stored in bf16; D = rowdot(dO, O) then
+    # takes the rounded O) against the fp64 oracle at the bf16 contract
+    # tolerances, on the DeBERTa and Transformer-XL recipes
+    spec, arr = scaled_config(idx, B=1, H=2, N=N)
+    _case(f"cfg{idx}-N{N}-bf16out", spec, arr, out_dtype="bf16")
+
+
+def test_bf16_outputs_t5_against_oracle():
+    # T5 at tau = 1: |dQ|, |dK| and |dBias| reach ~20-30, where bf16's spacing
+    # is 0.125, so one rounding of a stored dQ or dK alone can exceed 2e-2
+    # absolute, and D = rowdot(dO, O) from the rounded O moves dQ, dK and
+    # dBias by up to ~0.1 (a CPU simulation of both roundings on this recipe
+    # gives 5e-2 and 1e-1).  The relative L2 bound holds for every output and
+    # the absolute bound for O and dV; dQ, dK and dBias are held to 2e-2 plus
+    # the stored value's own rounding (2^-8 of it, dQ and dK) plus what D's
+    # rounding can move them by: with e_i = 2^-8 sum_d |dO_id| |O_id|
+    # bounding the change of D_i (G_ij moves by P_ij times it), dQ_i moves by
+    # at most e_i (P |K|)_i, dK_j by (P^T (e |Q|))_j and dBias[r] by the sum of
+    # P_ij e_i over the pairs in bucket r.
+    from oracle.attention import slice_forward
+    spec, arr = scaled_config(2, B=1, H=2, N=300)
+    got = run_library(spec, arr, out_dtype="bf16")
+    ref = oracle.forward_backward(spec, arr)
+    check(spec, got, ref, keys=["o", "dv"], label="cfg2-bf16out")
+    rows = oracle.relation_rows(spec, "bias")
+    R = spec["rows"]
+    for h in range(spec["H"]):
+        p = slice_forward(spec, arr, 0, h)[2]
+        e = 2.0 ** -8 * np.sum(np.abs(arr["do"][0, h]) * np.abs(ref["o"][0, h]), axis=1,
+                               keepdims=True)
+        moved = {"dq": e * (p @ np.abs(arr["k"][0, h])),
+                 "dk": p.T @ (e * np.abs(arr["q"][0, h])),
+                 "dbias": np.bincount(rows.ravel(), weights=(p * e).ravel(), minlength=R)}
+        for key in ("dq", "dk", "dbias"):
+            if key == "dbias":
+                r, g, own = ref[key][:, h], got[key][:, h], 0.0
+            else:
+                r, g = ref[key][0, h], got[key][0, h]
+                own = 2.0 ** -8 * np.abs(r)
+            ma, rl = errors(g, r)
+            print(f"cfg2-bf16out h{h} {key:5s} max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+            assert rl <= 1e-2, key
+            assert np.all(np.abs(g - r) <= 2e-2 + own + moved[key]), key
 
 
 def test_recompute_projections_same_bits():
