@@ -62,6 +62,11 @@ extern "C" {
 #define RELPOS_MAP_LOG_BUCKET 3 /* DeBERTa-v3 log buckets (bucket_size,     */
                                 /* max_position); row = clip(bkt(x)+bs,0,2bs-1) */
 #define RELPOS_MAP_EXPLICIT 4   /* row = explicit_rows[clip(x,-clip,clip)+clip] */
+/* Any map of the offset alone is accepted, including maps whose rows are not
+   one interval of offsets (e.g. x and -x sharing a row, [RPA] "Atomic
+   fallback"): the bucket copy gives every offset its own expanded row, and a
+   table row's gradient is the fixed-order sum over its copies, so no atomics
+   are needed for them either. */
 
 /* ---- dtypes ------------------------------------------------------------ */
 #define RELPOS_DTYPE_F32 0

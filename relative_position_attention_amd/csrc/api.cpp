@@ -202,9 +202,34 @@ int build_groups(const Plan& p, void* z, hipStream_t s) {
   return RELPOS_OK;
 }
 
+// Host-built int32 metadata written to device memory as kernel arguments
+// (no host-to-device copy).
+int upload(const std::vector<int32_t>& v, int32_t* dst, hipStream_t s) {
+  const int n = static_cast<int>(v.size());
+  for (int k0 = 0; k0 < n; k0 += kMetaChunk) {
+    MetaChunk c;
+    c.dst = dst + k0;
+    c.count = std::min(kMetaChunk, n - k0);
+    std::memcpy(c.vals, v.data() + k0, sizeof(int32_t) * c.count);
+    RP_HIP(launch_meta_fill(c, s));
+  }
+  return RELPOS_OK;
+}
+
+const int32_t* fold_ptr(const Plan& p, void* ws, int idx) {
+  return at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(idx) * std::max(p.R, 1) * 2;
+}
+
+// Index list of table idx's fold, or null when its rows are intervals.
+int32_t* fold_list_ptr(const Plan& p, void* ws, int idx) {
+  if (!p.fold_listed[idx]) return nullptr;
+  return at_off<int32_t>(ws, p.ws_fold_list) + static_cast<size_t>(idx) * p.S;
+}
+
 // Expanded row maps and (with_fold: only the backward's table-gradient folds
-// read them) fold intervals, built on the device into ws.
+// read them) fold intervals or index lists, written into ws.
 int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
+  int rc;
   struct Tab {
     bool on;
     const std::vector<int32_t>* beta;
@@ -218,7 +243,7 @@ int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
   for (auto& t : tabs) {
     if (!t.on) continue;
     int32_t* beta = at_off<int32_t>(ws, t.beta_off);
-    if (p.affine_map) {
+    if (p.affine_map) {  // identity and clipped rows are always intervals
       AffineMapArgs a;
       a.beta = beta;
       a.kind = p.map_kind;
@@ -233,24 +258,21 @@ int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
     } else {
       // bucketed / explicit maps: the host-built rows travel as kernel
       // arguments (no host-to-device copy)
-      for (int k0 = 0; k0 < p.S; k0 += kMetaChunk) {
-        MetaChunk c;
-        c.dst = beta + k0;
-        c.count = std::min(kMetaChunk, p.S - k0);
-        std::memcpy(c.vals, t.beta->data() + k0, sizeof(int32_t) * c.count);
-        RP_HIP(launch_meta_fill(c, s));
-      }
+      if ((rc = upload(*t.beta, beta, s)) != RELPOS_OK) return rc;
     }
     if (with_fold) {
       int32_t* fold = at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(t.fold_idx) * R * 2;
-      RP_HIP(launch_fold_meta(beta, fold, p.S, R, s));
+      if (p.fold_listed[t.fold_idx]) {
+        // rows that are not intervals: the host-built positions and list
+        if ((rc = upload(p.fold_rows[t.fold_idx], fold, s)) != RELPOS_OK) return rc;
+        if ((rc = upload(p.fold_list[t.fold_idx], fold_list_ptr(p, ws, t.fold_idx), s)) != RELPOS_OK)
+          return rc;
+      } else {
+        RP_HIP(launch_fold_meta(beta, fold, p.S, R, s));
+      }
     }
   }
   return RELPOS_OK;
-}
-
-const int32_t* fold_ptr(const Plan& p, void* ws, int idx) {
-  return at_off<int32_t>(ws, p.ws_fold) + static_cast<size_t>(idx) * std::max(p.R, 1) * 2;
 }
 
 int expand_tables(const Plan& p, const relpos_desc* desc, const relpos_tensors* in, void* ws,
@@ -320,7 +342,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.S = p.S;
     pa.NG = p.NG;
     if (dt == 0)
-      RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zq), s));
+      RP_HIP(launch_project_f32(pa, p.BH, max_pitch(p.zq), s));
     else
       RP_HIP(launch_project_bf16(pa, p.BH, s));
   }
@@ -339,7 +361,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     pa.S = p.S;
     pa.NG = p.NG;
     if (dt == 0)
-      RP_HIP(launch_project(dt, pa, p.BH, max_pitch(p.zk), s));
+      RP_HIP(launch_project_f32(pa, p.BH, max_pitch(p.zk), s));
     else
       RP_HIP(launch_project_bf16(pa, p.BH, s));
   }
@@ -452,7 +474,7 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int ff = base_flags(p) | (p.split ? F_SPLIT : 0);
   RP_MARK(0);
   if (p.dtype == RELPOS_DTYPE_F32)
-    RP_HIP(launch_attn_fwd(0, ff, a, p.B, s));
+    RP_HIP(launch_attn_fwd_f32(ff, a, p.B, s));
   else
     RP_HIP(launch_attn_fwd_bf16(ff, a, p.B, s));
   RP_MARK(1);
@@ -534,7 +556,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0) |
                      (p.dzq_f16 ? F_DZ16 : 0);
   if (dt == 0)
-    RP_HIP(launch_attn_bwd_q(dt, qflags, a, p.B, s));
+    RP_HIP(launch_attn_bwd_q_f32(qflags, a, p.B, s));
   else
     RP_HIP(launch_bwd_q_bf16(qflags, a, p.B, s));
   RP_MARK(2);
@@ -559,7 +581,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.dz_f32 = p.dzq_f32;
     f.dz_f16 = p.dzq_f16;
     if (dt == 0)
-      RP_HIP(launch_finalize(dt, f, p.BH, s));
+      RP_HIP(launch_finalize_f32(f, p.BH, s));
     else
       RP_HIP(launch_finalize_bf16(f, p.BH, s));
   }
@@ -583,7 +605,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.dz_f32 = p.dzq_f32;
     pa.dz_f16 = p.dzq_f16;
     if (dt == 0)
-      RP_HIP(launch_partials(dt, pa, s));
+      RP_HIP(launch_partials_f32(pa, s));
     else
       RP_HIP(launch_partials_bf16(pa, s));
     if (p.aq) {
@@ -591,6 +613,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
       fa.p1 = p1;
       fa.p2 = p2;
       fa.fold = fold_ptr(p, ws, 0);
+      fa.list = fold_list_ptr(p, ws, 0);
       fa.vb = p.v ? in->vbias : nullptr;
       fa.out = gr->daq;
       fa.row_stride = desc->aq_row_stride;
@@ -608,6 +631,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
       FoldBiasArgs fb;
       fb.db = db;
       fb.fold = fold_ptr(p, ws, 2);
+      fb.list = fold_list_ptr(p, ws, 2);
       fb.out = gr->dbias;
       fb.row_stride = desc->bias_row_stride;
       fb.head_stride = desc->bias_head_stride;
@@ -633,7 +657,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   const int kflags = bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0);
   RP_MARK(3);
   if (dt == 0)
-    RP_HIP(launch_attn_bwd_k(dt, kflags, a, p.B, s));
+    RP_HIP(launch_attn_bwd_k_f32(kflags, a, p.B, s));
   else
     RP_HIP(launch_bwd_k_bf16(kflags, a, p.B, s));
   RP_MARK(4);
@@ -658,7 +682,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     f.causal = p.causal;
     f.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
     if (dt == 0)
-      RP_HIP(launch_finalize(dt, f, p.BH, s));
+      RP_HIP(launch_finalize_f32(f, p.BH, s));
     else
       RP_HIP(launch_finalize_bf16(f, p.BH, s));
   }
@@ -682,13 +706,14 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     pa.dz_f32 = 0;
     pa.dz_f16 = 0;
     if (dt == 0)
-      RP_HIP(launch_partials(dt, pa, s));
+      RP_HIP(launch_partials_f32(pa, s));
     else
       RP_HIP(launch_partials_bf16(pa, s));
     FoldArgs fa;
     fa.p1 = p1;
     fa.p2 = nullptr;
     fa.fold = fold_ptr(p, ws, 1);
+    fa.list = fold_list_ptr(p, ws, 1);
     fa.vb = nullptr;
     fa.out = gr->dak;
     fa.row_stride = desc->ak_row_stride;

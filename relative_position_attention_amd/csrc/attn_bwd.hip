@@ -1,5 +1,6 @@
-// Backward attention passes ([RPA] Table 9 "Query-parallel pass" and
-// "Key-parallel pass", Algorithm 2).  [RPA] = "Fast and Exact Relative-
+// Backward attention passes for fp32 inputs ([RPA] Table 9 "Query-parallel
+// pass" and "Key-parallel pass", Algorithm 2; bf16 inputs run bwd_q_fast.hip
+// and bwd_k_fast.hip).  [RPA] = "Fast and Exact Relative-
 // Position Attention via Structure-Aware Kernels" (arXiv 2611.01182).
 //
 // Both passes rebuild each score tile from the saved logsumexp L and
@@ -39,7 +40,6 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZQ) != 0;
-  constexpr bool SPLIT = (F & F_SPLIT) != 0 && sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T lds[2][3][64 * P];  // K rows, K^T, V rows
 
   const int tid = threadIdx.x;
@@ -201,20 +201,14 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
     // dQ^T += K^T G^T
 #pragma unroll
     for (int c = 0; c < NST; ++c) {
-      Frag gf[2], gl[2];
+      Frag gf[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        gf[qb] = frag_regs<T, 4>(gv[qb], c);
-        if constexpr (SPLIT) gl[qb] = frag_regs_lo<T, 4>(gv[qb], c);
-      }
+      for (int qb = 0; qb < 2; ++qb) gf[qb] = frag_regs<T, 4>(gv[qb], c);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         Frag kf = frag_perm<T>(Kt, 16 * db + c16, c, g);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          dq[qb][db] = M::run(kf, gf[qb], dq[qb][db]);
-          if constexpr (SPLIT) dq[qb][db] = M::run(kf, gl[qb], dq[qb][db]);
-        }
+        for (int qb = 0; qb < 2; ++qb) dq[qb][db] = M::run(kf, gf[qb], dq[qb][db]);
       }
     }
 
@@ -259,7 +253,6 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
-  constexpr bool SPLIT = (F & F_SPLIT) != 0 && sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * P];  // Q rows, Q^T, dO rows, dO^T
 
   const int tid = threadIdx.x;
@@ -439,15 +432,11 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
     // dV^T += dO^T P ; dK^T += Q^T G
 #pragma unroll
     for (int c = 0; c < NST; ++c) {
-      Frag pf[2], pl[2], gf[2], gl[2];
+      Frag pf[2], gf[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         pf[kb] = frag_regs<T, 4>(pv[kb], c);
         gf[kb] = frag_regs<T, 4>(gv[kb], c);
-        if constexpr (SPLIT) {
-          pl[kb] = frag_regs_lo<T, 4>(pv[kb], c);
-          gl[kb] = frag_regs_lo<T, 4>(gv[kb], c);
-        }
       }
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -456,9 +445,7 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           dvacc[kb][db] = M::run(da, pf[kb], dvacc[kb][db]);
-          if constexpr (SPLIT) dvacc[kb][db] = M::run(da, pl[kb], dvacc[kb][db]);
           dkacc[kb][db] = M::run(qa, gf[kb], dkacc[kb][db]);
-          if constexpr (SPLIT) dkacc[kb][db] = M::run(qa, gl[kb], dkacc[kb][db]);
         }
       }
     }
@@ -518,15 +505,15 @@ hipError_t launch_k(const AttnArgs& a, int B, hipStream_t s) {
   X(F_ZQ | F_DZQ | F_DZ32) X(F_BT | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_DZQ | F_DZ32) \
   X(F_ZK | F_BT | F_DZQ | F_DZ32)
 
-template <typename T, int SPL>
+template <typename T>
 hipError_t dispatch_q(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZQ | F_DZ32);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \
-    return launch_q<T, (X) | SPL>(a, B, s);          \
+    return launch_q<T, (X)>(a, B, s);          \
   case (X) | F_CAUSAL:                               \
-    return launch_q<T, (X) | F_CAUSAL | SPL>(a, B, s);
+    return launch_q<T, (X) | F_CAUSAL>(a, B, s);
     RP_QFLAGS(RP_CASE)
 #undef RP_CASE
     default:
@@ -539,15 +526,15 @@ hipError_t dispatch_q(int flags, const AttnArgs& a, int B, hipStream_t s) {
   X(F_U) X(F_ZQ | F_U) X(F_BT | F_U) X(F_ZQ | F_ZK | F_DZK | F_U) X(F_ZK | F_DZK | F_U) \
   X(F_ZK | F_BT | F_DZK | F_U)
 
-template <typename T, int SPL>
+template <typename T>
 hipError_t dispatch_k(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZK | F_U);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \
-    return launch_k<T, (X) | SPL>(a, B, s);          \
+    return launch_k<T, (X)>(a, B, s);          \
   case (X) | F_CAUSAL:                               \
-    return launch_k<T, (X) | F_CAUSAL | SPL>(a, B, s);
+    return launch_k<T, (X) | F_CAUSAL>(a, B, s);
     RP_KFLAGS(RP_CASE)
 #undef RP_CASE
     default:
@@ -557,17 +544,12 @@ hipError_t dispatch_k(int flags, const AttnArgs& a, int B, hipStream_t s) {
 
 }  // namespace
 
-// The hi/lo split of G only exists for bf16 (fp32 MFMA keeps G whole).
-hipError_t launch_attn_bwd_q(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (dtype == 0) return dispatch_q<float, 0>(flags, a, B, s);
-  if (flags & F_SPLIT) return dispatch_q<bf16, F_SPLIT>(flags, a, B, s);
-  return dispatch_q<bf16, 0>(flags, a, B, s);
+hipError_t launch_attn_bwd_q_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  return dispatch_q<float>(flags, a, B, s);
 }
 
-hipError_t launch_attn_bwd_k(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (dtype == 0) return dispatch_k<float, 0>(flags, a, B, s);
-  if (flags & F_SPLIT) return dispatch_k<bf16, F_SPLIT>(flags, a, B, s);
-  return dispatch_k<bf16, 0>(flags, a, B, s);
+hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  return dispatch_k<float>(flags, a, B, s);
 }
 
 }  // namespace relpos

@@ -1,4 +1,5 @@
-// Forward attention kernel ([RPA] Table 9 "Attention"; the forward of Algorithm 1).
+// Forward attention kernel for fp32 inputs ([RPA] Table 9 "Attention"; the
+// forward of Algorithm 1; bf16 inputs run fwd_fast.hip).
 // [RPA] = "Fast and Exact Relative-Position Attention via Structure-Aware
 // Kernels" (arXiv 2611.01182).
 //
@@ -32,7 +33,6 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NST = 64 / KS;
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
-  constexpr bool SPLIT = (F & F_SPLIT) != 0 && sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T lds[2][2][64 * P];
 
   const int tid = threadIdx.x;
@@ -173,20 +173,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < NST; ++c) {
-      Frag pf[2], pl[2];
+      Frag pf[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        pf[qb] = frag_regs<T, 4>(x[qb], c);
-        if constexpr (SPLIT) pl[qb] = frag_regs_lo<T, 4>(x[qb], c);
-      }
+      for (int qb = 0; qb < 2; ++qb) pf[qb] = frag_regs<T, 4>(x[qb], c);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         Frag vf = frag_perm<T>(Vt, 16 * db + c16, c, g);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          o[qb][db] = M::run(vf, pf[qb], o[qb][db]);
-          if constexpr (SPLIT) o[qb][db] = M::run(vf, pl[qb], o[qb][db]);
-        }
+        for (int qb = 0; qb < 2; ++qb) o[qb][db] = M::run(vf, pf[qb], o[qb][db]);
       }
     }
 
@@ -220,13 +214,13 @@ hipError_t launch_one(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int SPL>
+template <typename T>
 hipError_t dispatch(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL);
   switch (f) {
 #define RP_CASE(X) \
   case X:          \
-    return launch_one<T, (X) | SPL>(a, B, s);
+    return launch_one<T, (X)>(a, B, s);
     RP_CASE(0)
     RP_CASE(F_ZQ)
     RP_CASE(F_ZK)
@@ -247,10 +241,8 @@ hipError_t dispatch(int flags, const AttnArgs& a, int B, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_fwd(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (dtype == 0) return dispatch<float, 0>(flags, a, B, s);
-  if (flags & F_SPLIT) return dispatch<bf16, F_SPLIT>(flags, a, B, s);
-  return dispatch<bf16, 0>(flags, a, B, s);
+hipError_t launch_attn_fwd_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  return dispatch<float>(flags, a, B, s);
 }
 
 }  // namespace relpos

@@ -599,7 +599,8 @@ __global__ __launch_bounds__(256) void fold_table_kernel(FoldArgs f, int dtype) 
   const int n = sb >= sa ? (sb - sa + 1) * nh * f.nchunk : 0;
   auto item = [&](int it) {
     const int c = it % f.nchunk, rest = it / f.nchunk;
-    const int h = h0 + rest % nh, s = sa + rest / nh;
+    const int h = h0 + rest % nh, pos = sa + rest / nh;
+    const int s = f.list != nullptr ? f.list[pos] : pos;
     const int64_t base = (static_cast<int64_t>(h) * f.nchunk + c) * f.S + s;
     float v = f.p1[base * 64 + d];
     if (f.vb != nullptr) {
@@ -637,14 +638,16 @@ __global__ __launch_bounds__(256) void p2_sum_kernel(const float* p2, float* db,
 }
 
 // dbias[r, h] = sum over the copies s of row r (ascending) of db[h][s]: the
-// bucket fold of [RPA] App. B.1 (bucket-copy lemma), db = E^T db~
+// bucket fold of [RPA] App. B.1 (bucket-copy lemma), db = E^T db~; the copies
+// are an interval of s, or listed when the row's offsets are not contiguous
 __global__ __launch_bounds__(256) void fold_bias_kernel(FoldBiasArgs f) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= f.R * f.H) return;
   const int r = idx / f.H, h = idx % f.H;
   const int sa = f.fold[2 * r], sb = f.fold[2 * r + 1];
   float sum = 0.f;
-  for (int s = sa; s <= sb; ++s) sum += f.db[static_cast<int64_t>(h) * f.S + s];
+  for (int pos = sa; pos <= sb; ++pos)
+    sum += f.db[static_cast<int64_t>(h) * f.S + (f.list != nullptr ? f.list[pos] : pos)];
   f.out[r * f.row_stride + h * f.head_stride] = sum;
 }
 
@@ -781,12 +784,9 @@ hipError_t launch_bias_expand(int dtype, const BiasExpandArgs& e, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_project(int dtype, const ProjectArgs& p, int BH, int max_pitch, hipStream_t s) {
+hipError_t launch_project_f32(const ProjectArgs& p, int BH, int max_pitch, hipStream_t s) {
   dim3 grid(nblk(max_pitch, 64), nblk(p.N, 64), BH);
-  if (dtype == 0)
-    hipLaunchKernelGGL(project_kernel<float>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(project_kernel<bf16>, grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL(project_kernel<float>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -817,25 +817,15 @@ hipError_t launch_rowdot(int dtype, int out_f32, const void* o, const void* dout
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s) {
+hipError_t launch_finalize_f32(const FinalizeArgs& f, int BH, hipStream_t s) {
   dim3 grid(nblk(f.N, 64), BH);
-  if (dtype == 0)
-    hipLaunchKernelGGL((finalize_kernel<float, float>), grid, dim3(256), 0, s, f);
-  else if (f.dz_f32)
-    hipLaunchKernelGGL((finalize_kernel<bf16, float>), grid, dim3(256), 0, s, f);
-  else
-    hipLaunchKernelGGL((finalize_kernel<bf16, bf16>), grid, dim3(256), 0, s, f);
+  hipLaunchKernelGGL((finalize_kernel<float, float>), grid, dim3(256), 0, s, f);
   return hipGetLastError();
 }
 
-hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s) {
+hipError_t launch_partials_f32(const PartialArgs& p, hipStream_t s) {
   dim3 grid(nblk(p.S, 64), p.H, p.nchunk);
-  if (dtype == 0)
-    hipLaunchKernelGGL((partials_kernel<float, float>), grid, dim3(256), 0, s, p);
-  else if (p.dz_f32)
-    hipLaunchKernelGGL((partials_kernel<bf16, float>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((partials_kernel<bf16, bf16>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((partials_kernel<float, float>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -59,12 +59,13 @@ struct AttnArgs {
   int out_f32;
 };
 
-// dtype: 0 = fp32 inputs, 1 = bf16 inputs.  Return hipError_t of the launch.
-hipError_t launch_attn_fwd(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+// Each launcher returns the hipError_t of its launch.
+// fp32 inputs: 16x16x4 fp32 MFMA, plain loads (attn_fwd.hip, attn_bwd.hip)
+hipError_t launch_attn_fwd_f32(int flags, const AttnArgs& a, int B, hipStream_t s);
 // bf16 forward: 64 queries per wave, 256 per workgroup (fwd_fast.hip)
 hipError_t launch_attn_fwd_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
-hipError_t launch_attn_bwd_q(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
-hipError_t launch_attn_bwd_k(int dtype, int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_bwd_q_f32(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_t s);
 // bf16 backward passes: 32 tokens per wave, buffer loads, transposing LDS
 // reads (bwd_q_fast.hip, bwd_k_fast.hip)
 hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
@@ -134,7 +135,7 @@ struct ProjectArgs {
   int64_t z_bh;
   int N, H, D, S, NG;
 };
-hipError_t launch_project(int dtype, const ProjectArgs& p, int BH, int max_pitch, hipStream_t s);
+hipError_t launch_project_f32(const ProjectArgs& p, int BH, int max_pitch, hipStream_t s);
 // bf16 inputs: row-walking projection with LDS-staged table tiles
 hipError_t launch_project_bf16(const ProjectArgs& p, int BH, hipStream_t s);
 
@@ -176,7 +177,7 @@ struct FinalizeArgs {
   int dz_f32;  // entries are fp32
   int dz_f16;  // entries are fp16
 };
-hipError_t launch_finalize(int dtype, const FinalizeArgs& f, int BH, hipStream_t s);
+hipError_t launch_finalize_f32(const FinalizeArgs& f, int BH, hipStream_t s);
 // bf16: aligned 16-byte staging of the offset gradients (reduce_fast.hip)
 hipError_t launch_finalize_bf16(const FinalizeArgs& f, int BH, hipStream_t s);
 
@@ -195,16 +196,18 @@ struct PartialArgs {
   int dz_f32;     // entries are fp32 (scalar bias without a query table)
   int dz_f16;     // entries are fp16 (the Transformer-XL v term)
 };
-hipError_t launch_partials(int dtype, const PartialArgs& p, hipStream_t s);
+hipError_t launch_partials_f32(const PartialArgs& p, hipStream_t s);
 hipError_t launch_partials_bf16(const PartialArgs& p, hipStream_t s);
 
 // Second kernel: fixed-order sums over chunks (and heads of a shared table),
 // then the bucket fold dA[r] = sum over copies s of r ([RPA] App. B.1
-// bucket-copy lemma), written with the table's strides.
+// bucket-copy lemma), written with the table's strides.  A row's copies are
+// the interval fold[r] of s, or, with a list, list[fold[r]] (ascending s).
 struct FoldArgs {
   const float* p1;
   const float* p2;
-  const int32_t* fold;  // [R, 2] intervals
+  const int32_t* fold;  // [R, 2] intervals of expanded rows, or of positions in list
+  const int32_t* list;  // null, or expanded rows grouped by table row
   const void* vb;       // v bias [H, 64] (query side with V), else null
   float* out;
   int64_t row_stride, head_stride;
@@ -218,7 +221,8 @@ hipError_t launch_p2_sum(const float* p2, float* db, int H, int S, int nchunk, h
 // dbias[r, h] = sum over the copies of row r of db[h][s] (bucket fold)
 struct FoldBiasArgs {
   const float* db;      // [H, S]
-  const int32_t* fold;  // [R, 2] intervals
+  const int32_t* fold;  // [R, 2] intervals of expanded rows, or of positions in list
+  const int32_t* list;  // null, or expanded rows grouped by table row
   float* out;
   int64_t row_stride, head_stride;
   int H, R, S;

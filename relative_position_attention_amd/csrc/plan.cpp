@@ -179,9 +179,11 @@ bool saturation(const relpos_map& mp, int sign, int N, bool causal, int& D) {
   return true;
 }
 
-// Every table row must cover one interval of offsets ([RPA] "Atomic
-// fallback": the atomic-free path needs contiguous rows; maps failing it are
-// rejected here instead of falling back to atomics).
+// Whether every table row covers one interval of expanded rows.  The
+// bucket-copy expansion gives each offset its own expanded row, so the
+// backward never needs this ([RPA] "Atomic fallback" accumulates such maps
+// with atomics instead): a row's gradient is the fixed-order sum over its
+// copies, read through an index list when they are not one interval.
 bool contiguous(const std::vector<int32_t>& beta, int R) {
   std::vector<int> last(std::max(R, 1), -2);
   for (size_t s = 0; s < beta.size(); ++s) {
@@ -191,6 +193,32 @@ bool contiguous(const std::vector<int32_t>& beta, int R) {
     last[r] = static_cast<int>(s);
   }
   return true;
+}
+
+// Fold index of a table whose rows are not intervals: list = the reachable
+// expanded rows s grouped by table row (ascending r, then ascending s), and
+// fold[2r], fold[2r+1] = first and last position of row r in list ([1, 0]
+// for a row no offset reaches).
+void fold_index(const std::vector<int32_t>& beta, int R, std::vector<int32_t>& fold,
+                std::vector<int32_t>& list) {
+  const int Rm = std::max(R, 1);
+  std::vector<int32_t> count(Rm, 0);
+  for (int32_t r : beta)
+    if (r >= 0) ++count[r];
+  fold.assign(2 * static_cast<size_t>(Rm), 0);
+  int pos = 0;
+  for (int r = 0; r < Rm; ++r) {
+    fold[2 * r] = count[r] ? pos : 1;
+    fold[2 * r + 1] = count[r] ? pos + count[r] - 1 : 0;
+    pos += count[r];
+  }
+  list.assign(pos, 0);
+  std::vector<int32_t> fill(Rm, 0);
+  for (size_t s = 0; s < beta.size(); ++s) {
+    const int r = beta[s];
+    if (r < 0) continue;
+    list[fold[2 * r] + fill[r]++] = static_cast<int32_t>(s);
+  }
 }
 
 bool build_side(Plan& p, bool query_side, std::string& detail) {
@@ -397,9 +425,15 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   if ((rc = expand(p.aq, desc->sign_q, p.beta_q)) != RELPOS_OK) return rc;
   if ((rc = expand(p.ak, desc->sign_k, p.beta_k)) != RELPOS_OK) return rc;
   if ((rc = expand(p.bias, desc->sign_b, p.beta_b)) != RELPOS_OK) return rc;
-  if (!contiguous(p.beta_q, p.R) || !contiguous(p.beta_k, p.R) || !contiguous(p.beta_b, p.R)) {
-    detail = "a relation row covers more than one interval of offsets (non-contiguous map)";
-    return RELPOS_E_UNSUPPORTED_MAP;
+  // rows that are not one interval of offsets (e.g. delta and -delta sharing a
+  // row): their gradient folds read an index list built here
+  {
+    const std::vector<int32_t>* betas[3] = {&p.beta_q, &p.beta_k, &p.beta_b};
+    const bool on[3] = {p.aq, p.ak, p.bias};
+    for (int t = 0; t < 3; ++t) {
+      p.fold_listed[t] = on[t] && !contiguous(*betas[t], p.R);
+      if (p.fold_listed[t]) fold_index(*betas[t], p.R, p.fold_rows[t], p.fold_list[t]);
+    }
   }
   p.map_kind = desc->map.kind;
   p.affine_map = desc->map.kind == RELPOS_MAP_IDENTITY || desc->map.kind == RELPOS_MAP_CLIPPED;
@@ -484,6 +518,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   off = align256(off + 4 * p.S);
   p.ws_fold = off;  // three [R, 2] interval tables (A^Q, A^K, b)
   off = align256(off + 3 * static_cast<size_t>(std::max(p.R, 1)) * 2 * 4);
+  p.ws_fold_list = off;  // three [S] index lists (tables with listed folds)
+  off = align256(off + 3 * static_cast<size_t>(p.S) * 4);
   if (p.aq) {
     p.ws_atq = off;
     off = align256(off + static_cast<size_t>(p.Htq) * p.S * kHeadDim * p.t_size);

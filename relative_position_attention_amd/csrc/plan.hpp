@@ -48,12 +48,17 @@ struct Plan {
   size_t dz_entry = 2;     // bytes per entry of the shared offset-gradient buffer
   bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
+  // Per table (A^Q, A^K, b): rows that are not one interval of expanded rows
+  // fold through an index list (fold_rows: [R, 2] first / last position of
+  // each row in fold_list; fold_list: expanded rows grouped by table row).
+  bool fold_listed[3] = {false, false, false};
+  std::vector<int32_t> fold_rows[3], fold_list[3];
 
   // ---- byte offsets inside z ----
   size_t z_gq = 0, z_gk = 0, z_zq = 0, z_zk = 0, z_rowlo = 0, z_rowhi = 0, z_keylo = 0, z_keyhi = 0,
          z_keymid = 0, z_bt = 0, z_bytes = 0;
   // ---- byte offsets inside ws (forward part) ----
-  size_t ws_beta_q = 0, ws_beta_k = 0, ws_beta_b = 0, ws_fold = 0,
+  size_t ws_beta_q = 0, ws_beta_k = 0, ws_beta_b = 0, ws_fold = 0, ws_fold_list = 0,
          ws_atq = 0, ws_atk = 0, ws_fwd_end = 0;
   // ---- byte offsets inside ws (backward part, after ws_fwd_end) ----
   size_t ws_D = 0, ws_dqacc = 0, ws_dkacc = 0, ws_dz = 0, ws_bndq = 0, ws_bndk = 0,

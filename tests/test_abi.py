@@ -126,17 +126,22 @@ def test_validation_errors():
 
 
 @needs_lib
-def test_noncontiguous_map_rejected():
-    # a map giving delta and -delta the same row is not contiguous ([RPA]
-    # "Atomic fallback"); the library rejects it instead of using atomics
-    spec = _spec_small(1, 64)
-    spec = copy.deepcopy(spec)
+@pytest.mark.parametrize("rows", [[3, 2, 1, 0, 1, 2, 3], [2, 0, 3, 1, 0, 2, 3]],
+                         ids=["symmetric", "scattered"])
+def test_noncontiguous_map_plan(rows):
+    # maps whose table rows are not one interval of offsets (delta and -delta
+    # sharing a row, or rows scattered over the offsets; [RPA] "Atomic
+    # fallback") are planned like any other: the expanded rows are the map
+    # itself, beta(s) = phi(s - D)
+    spec = copy.deepcopy(_spec_small(1, 64))
     c = 3
-    spec["map"] = {"kind": "explicit", "clip": c, "rows": [abs(x) for x in range(-c, c + 1)]}
-    spec["rows"] = c + 1
-    with pytest.raises(rpa.RelposError) as ei:
-        rpa.plan_sizes(rpa.Problem(spec))
-    assert ei.value.code == -3
+    spec["map"] = {"kind": "explicit", "clip": c, "rows": rows}
+    spec["rows"] = 4
+    prob = rpa.Problem(spec)
+    D = prob.sizes()["delta"]
+    s = np.arange(2 * D + 1)
+    want = oracle.map_rows(spec["map"], spec["signs"]["aq"] * (s - D))
+    assert rpa.plan_rows(prob, 0) == list(want)
 
 
 @needs_lib

@@ -129,6 +129,42 @@ def test_term_combinations(terms, causal):
     _case(f"{spec['name']}-causal{int(causal)}", spec, arr)
 
 
+# Maps whose table rows are not one interval of offsets ([RPA] "Atomic
+# fallback"): delta and -delta sharing a row, and rows scattered over the
+# offsets.  The library folds each row's expanded rows through an index list
+# (no atomics).
+_NONCONTIG = {
+    "symmetric": (5, [abs(x) for x in range(-5, 6)], 6),
+    "scattered": (6, [3, 0, 4, 1, 0, 2, 3, 1, 4, 0, 2, 1, 3], 5),
+}
+
+
+def _noncontig(name, terms, N, dtype, seed, causal):
+    clip, rows, R = _NONCONTIG[name]
+    spec, arr = make_mixed(terms, 1, 2, N, dtype, seed, causal=causal, clip=clip)
+    spec = copy.deepcopy(spec)
+    spec["map"] = {"kind": "explicit", "clip": clip, "rows": rows}
+    spec["rows"] = R
+    arr = dict(arr)
+    for key in ("aq", "ak", "bias"):
+        if key in arr:
+            arr[key] = np.ascontiguousarray(arr[key][:R])
+    return spec, arr
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("name", sorted(_NONCONTIG))
+def test_noncontiguous_maps_f32(name, causal):
+    spec, arr = _noncontig(name, ["aq", "ak", "bias", "u", "v"], 200, "f32", 13, causal)
+    _case(f"noncontig-{name}-f32-c{int(causal)}", spec, arr)
+
+
+@pytest.mark.parametrize("name", sorted(_NONCONTIG))
+def test_noncontiguous_maps_bf16(name):
+    spec, arr = _noncontig(name, ["aq", "ak", "bias"], 333, "bf16", 14, False)
+    _case(f"noncontig-{name}-bf16", spec, arr)
+
+
 def test_all_terms_bf16():
     spec, arr = make_mixed(["aq", "ak", "bias", "u", "v"], 2, 3, 333, "bf16", 12, causal=False)
     _case(spec["name"] + "-bf16", spec, arr)

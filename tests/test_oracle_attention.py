@@ -253,3 +253,22 @@ def test_dzq_row_sums_equal_bias_gradient():
     # dv = sum_r (sum_i dZ^Q[i,r]) a_r must equal sum_r db_r a_r
     a = arr["aq"]
     np.testing.assert_allclose(g2["dv_bias"][0], g["dbias"][:, 0] @ a, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_noncontiguous_map_bruteforce(causal):
+    # a map giving delta and -delta the same row ([RPA] "Atomic fallback"
+    # names such maps): the vectorised scatter by row equals the per-pair
+    # brute force for every term
+    from synth import make_mixed
+    spec, arr = make_mixed(["aq", "ak", "bias", "u", "v"], 1, 2, 9, "f32", 5, causal=causal,
+                           clip=3)
+    spec = copy.deepcopy(spec)
+    spec["map"] = {"kind": "explicit", "clip": 3, "rows": [3, 2, 1, 0, 1, 2, 3]}
+    spec["rows"] = 4
+    for key in ("aq", "ak", "bias"):
+        arr[key] = arr[key][:4].copy()
+    ref = oracle.brute_forward_backward(spec, arr)
+    got = oracle.forward_backward(spec, arr)
+    for key in ref:
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-10, atol=1e-12, err_msg=key)
