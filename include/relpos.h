@@ -188,6 +188,27 @@ int relpos_project(const relpos_desc *desc, const relpos_shape *shape,
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * relpos_project_noalloc -- relpos_project without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  It runs the same
+ * kernels as relpos_project; their workspace (row maps and expanded tables,
+ * relpos_sizes.fwd_ws_bytes) is a static device array of 64 MiB inside the
+ * library, one per GPU, held until the process ends.  The caller still owns
+ * the inputs and z; with z retained, relpos_attn_fwd needs no workspace, so
+ * the forward runs allocation-free.  Call it with the stream's device
+ * current.  Calls on one GPU share its array: calls that overlap on one GPU
+ * (several streams or threads) race and must be serialised by the caller.
+ * Nothing in the array needs clearing between calls (every entry read is
+ * written first by the same call).  Allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine).
+ * Errors: as relpos_project; WORKSPACE_TOO_SMALL when fwd_ws_bytes exceeds
+ * 64 MiB (e.g. an identity map over 2N - 1 offsets with many heads) or when
+ * z_bytes is too small; UNSUPPORTED for a device index above 63.
+ */
+int relpos_project_noalloc(const relpos_desc *desc, const relpos_shape *shape,
+                           const relpos_tensors *in, void *z, size_t z_bytes, void *stream);
+
+/*
  * relpos_attn_fwd -- [RPA] Table 9 "Attention" (the tiled loop of Algorithm 1):
  * the tiled online-softmax forward with offset-aware tiles (three key ranges
  * per query tile: saturated-high, band, saturated-low).  Writes

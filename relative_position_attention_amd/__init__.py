@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     plan_sizes,
     plan_rows,
     project,
+    project_noalloc,
     attn_fwd,
     attn_bwd,
     empty_grads,

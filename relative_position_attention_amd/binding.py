@@ -9,7 +9,7 @@ LIB_NAME = "librelpos.so"
 EXPORTED_SYMBOLS = (
     "relpos_plan_sizes", "relpos_plan_rows", "relpos_project", "relpos_attn_fwd",
     "relpos_attn_bwd", "relpos_strerror", "relpos_last_error", "relpos_abi_version",
-    "relpos_set_stage_events",
+    "relpos_set_stage_events", "relpos_project_noalloc",
 )
 
 ABI_VERSION = 2
@@ -90,6 +90,8 @@ def library():
         lib.relpos_project.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Shape),
                                        ctypes.POINTER(_Tensors), vp, ctypes.c_size_t, vp,
                                        ctypes.c_size_t, vp]
+        lib.relpos_project_noalloc.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Shape),
+                                               ctypes.POINTER(_Tensors), vp, ctypes.c_size_t, vp]
         lib.relpos_attn_fwd.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Shape),
                                         ctypes.POINTER(_Tensors), vp, ctypes.c_size_t, vp, vp,
                                         vp, ctypes.c_size_t, vp]
@@ -247,6 +249,16 @@ def project(problem, t, z=None, ws=None):
     _check(library().relpos_project(ctypes.byref(problem.desc), ctypes.byref(problem.shape),
                                     ctypes.byref(_tensors(problem, t)), _ptr(z), z.numel(),
                                     _ptr(ws), ws.numel(), _stream()), "relpos_project")
+    return z
+
+
+def project_noalloc(problem, t, z):
+    """relpos_project_noalloc: the projection into the caller's z with the
+    library's static scratch as workspace (no workspace argument)."""
+    _check(library().relpos_project_noalloc(ctypes.byref(problem.desc),
+                                            ctypes.byref(problem.shape),
+                                            ctypes.byref(_tensors(problem, t)), _ptr(z),
+                                            z.numel(), _stream()), "relpos_project_noalloc")
     return z
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -442,6 +443,53 @@ int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos
   return project_into(p, desc, in, z, ws, s);
 }
 
+// ---- allocation-free projection (relpos_project_noalloc)
+//
+// The workspace of relpos_project (row maps and expanded tables) lives in a
+// file-scope device array of fixed size, one copy per GPU for the life of the
+// process.  Host code never passes the array's name to a kernel: it is a
+// host-side stand-in, not a device address.  The device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  RP_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RELPOS_E_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(RELPOS_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RELPOS_OK;
+}
+
+int run_project_noalloc(const relpos_desc* desc, const relpos_shape* shape,
+                        const relpos_tensors* in, void* z, size_t z_bytes, hipStream_t s) {
+  int rc;
+  const Plan* pp = get_plan(desc, shape, rc);
+  if (pp == nullptr) return rc;
+  if (pp->ws_fwd_end > kScratchBytes)
+    return fail(RELPOS_E_WORKSPACE_TOO_SMALL,
+                "relpos_project_noalloc needs " + std::to_string(pp->ws_fwd_end) +
+                    " bytes of workspace; its static scratch holds " +
+                    std::to_string(kScratchBytes) + " (use relpos_project with a workspace)");
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != RELPOS_OK) return rc;
+  // every workspace entry the projection reads (row maps, expanded tables) is
+  // written by it first, so the previous call's contents need no clearing
+  return run_project(desc, shape, in, z, z_bytes, ws, kScratchBytes, s);
+}
+
 int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_tensors* in,
             const void* zc, size_t z_bytes, void* o, float* lse, void* ws, size_t ws_bytes,
             hipStream_t s) {
@@ -794,6 +842,15 @@ int relpos_project(const relpos_desc* desc, const relpos_shape* shape, const rel
                    void* z, size_t z_bytes, void* ws, size_t ws_bytes, void* stream) {
   try {
     return run_project(desc, shape, in, z, z_bytes, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(RELPOS_E_INVALID_ARG, "host error");
+  }
+}
+
+int relpos_project_noalloc(const relpos_desc* desc, const relpos_shape* shape,
+                           const relpos_tensors* in, void* z, size_t z_bytes, void* stream) {
+  try {
+    return run_project_noalloc(desc, shape, in, z, z_bytes, static_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(RELPOS_E_INVALID_ARG, "host error");
   }
