@@ -9,8 +9,25 @@ query biases written out as in the configurations' score formula:
                    + k_j . A^K[phi_K(i, j)]
                    + b[phi_b(i, j)] )  + M_ij
 
-(absent terms are zero; M_ij = -inf for j > i under the causal mask).  Then
+(absent terms are zero; M_ij = -inf for j > i under the causal mask, and
+for pairs in different segments under a segment mask).  Then
 P = softmax_row(S), O = P V and L_i = log sum_j exp(S_ij) ([RPA] §3.1 Eq. (1)).
+
+Masks and dropout ([RPA] appendix "Masks, packing, and dropout", which names
+padding masks, packed variable-length sequences and attention dropout without
+formulas; the readings here):
+  * segments: spec["segments"][b] lists disjoint token intervals [start, end)
+    of batch element b.  A pair is visible iff both tokens lie in the same
+    segment; tokens in no segment are padding.  One segment [0, L_b) is a
+    padding mask of length L_b; several segments in one row are packed
+    sequences.  Offsets stay delta = i - j (both tokens index the same row).
+    A query with no visible key has O = 0, L = -inf and no gradient.
+  * dropout: spec["dropout"] = {"p8": p8, "seed": seed} drops pair (i, j)
+    with probability p8 / 256 by the counter-based mask of ``philox`` and
+    scales the kept probabilities by 1 / (1 - p8 / 256): O = P~ V with
+    P~ = P * keep * scale, while L stays the logsumexp of S.  Backward:
+    dV = P~^T dO, dP = (dO V^T) * keep * scale, D_i = <dO_i, O_i>,
+    dS = P * (dP - D) (D_i = sum_j P_ij dP_ij still holds).
 
 Backward ([RPA] App. B.1, the dV/dS lemma): dV = P^T dO, dP = dO V^T,
 D_i = <dO_i, O_i>, dS = P * (dP - D).  With G = tau * dS the relation
@@ -29,6 +46,7 @@ by all heads).  Everything is float64.
 import numpy as np
 
 from .maps import relation_rows
+from .philox import keep_mask, keep_scale
 
 
 def _has(spec, term):
@@ -79,18 +97,47 @@ def slice_scores(spec, arrays, b, h, rows=None):
     s *= tau
     if spec["causal"]:
         s[np.triu_indices(N, 1)] = -np.inf
+    seg = segment_ids(spec, b)
+    if seg is not None:
+        s[(seg[:, None] != seg[None, :]) | (seg[:, None] < 0)] = -np.inf
     return s, rows
 
 
+def segment_ids(spec, b):
+    """Segment index of every token of batch element b (-1: padding), or None
+    without a segment mask."""
+    if spec.get("segments") is None:
+        return None
+    ids = np.full(spec["N"], -1, dtype=np.int64)
+    for k, (start, end) in enumerate(spec["segments"][b]):
+        assert 0 <= start <= end <= spec["N"] and np.all(ids[start:end] < 0), "bad segments"
+        ids[start:end] = k
+    return ids
+
+
+def dropout_of(spec, b, h):
+    """(keep mask, scale) of slice (b, h), or None without dropout."""
+    dr = spec.get("dropout")
+    if dr is None:
+        return None
+    return keep_mask(spec["N"], b * spec["H"] + h, dr["p8"], dr["seed"]), keep_scale(dr["p8"])
+
+
 def slice_forward(spec, arrays, b, h, rows=None):
-    """O (N x d) and natural-log L (N) of slice (b, h) ([RPA] §3.1 Eq. (1))."""
+    """O (N x d) and natural-log L (N) of slice (b, h) ([RPA] §3.1 Eq. (1)),
+    with the softmax P (before dropout).  A row with no visible key has P = 0,
+    O = 0 and L = -inf."""
     s, rows = slice_scores(spec, arrays, b, h, rows)
     m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)  # rows with no visible key
     e = np.exp(s - m)
     ssum = e.sum(axis=1, keepdims=True)
-    p = e / ssum
-    o = p @ arrays["v"][b, h]
-    lse = (m + np.log(ssum))[:, 0]
+    p = e / np.where(ssum > 0, ssum, 1.0)
+    dr = dropout_of(spec, b, h)
+    pd = p if dr is None else p * dr[0] * dr[1]
+    o = pd @ arrays["v"][b, h]
+    with np.errstate(divide="ignore"):
+        lse = (m + np.log(ssum))[:, 0]
     return o, lse, p, rows
 
 
@@ -106,12 +153,16 @@ def slice_forward_backward(spec, arrays, b, h, rows=None):
     N = spec["N"]
     R = spec.get("rows", 0)
     out = {"o": o, "lse": lse}
-    out["dv"] = p.T @ do                       # dV = P^T dO
+    dr = dropout_of(spec, b, h)
+    pd = p if dr is None else p * dr[0] * dr[1]
+    out["dv"] = pd.T @ do                      # dV = P~^T dO
     dp = do @ v.T                              # dP = dO V^T
+    if dr is not None:
+        dp = dp * dr[0] * dr[1]                # through the dropout mask
     dd = np.sum(do * o, axis=1, keepdims=True)  # D_i = <dO_i, O_i>
     ds = p * (dp - dd)                         # dS = P * (dP - D)
     g = tau * ds                               # every term of S carries tau
-    del p, dp, ds
+    del p, pd, dp, ds
     dq = g @ k
     kc = k
     dk = g.T @ (q + arrays["u"][h] if _has(spec, "u") else q)

@@ -12,10 +12,32 @@ import math
 import numpy as np
 
 from .maps import map_rows
+from .philox import philox4x32, keep_scale
 
 
 def _row(spec, term, i, j):
     return int(map_rows(spec["map"], np.array([spec["signs"][term] * (i - j)]))[0])
+
+
+def _visible(spec, b, i, j):
+    """Pair (i, j) of batch element b under the causal and segment masks."""
+    if spec["causal"] and j > i:
+        return False
+    segs = spec.get("segments")
+    if segs is None:
+        return True
+    return any(start <= i < end and start <= j < end for start, end in segs[b])
+
+
+def _kept(spec, bh, i, j):
+    """Dropout factor of pair (i, j): 0 if dropped, else the keep scale (one
+    Philox call per pair, the byte of the pair picked out of its block)."""
+    dr = spec.get("dropout")
+    if dr is None:
+        return 1.0
+    words = philox4x32(j >> 2, i >> 2, bh, 0, dr["seed"] & 0xFFFFFFFF, dr["seed"] >> 32)
+    byte = (int(words[i & 3]) >> (8 * (j & 3))) & 0xFF
+    return keep_scale(dr["p8"]) if byte >= dr["p8"] else 0.0
 
 
 def brute_forward_backward(spec, arrays):
@@ -54,7 +76,7 @@ def brute_forward_backward(spec, arrays):
             S = [[-math.inf] * N for _ in range(N)]
             for i in range(N):
                 for j in range(N):
-                    if spec["causal"] and j > i:
+                    if not _visible(spec, b, i, j):
                         continue
                     val = dot(q[i] + u, k[j])
                     if "aq" in terms:
@@ -65,22 +87,26 @@ def brute_forward_backward(spec, arrays):
                         val += arrays["bias"][_row(spec, "bias", i, j), h]
                     S[i][j] = tau * val
             P = [[0.0] * N for _ in range(N)]
+            X = [[_kept(spec, b * H + h, i, j) for j in range(N)] for i in range(N)]
             for i in range(N):
                 m = max(S[i])
+                if m == -math.inf:  # no visible key: O = 0, L = -inf
+                    out["lse"][b, h, i] = -math.inf
+                    continue
                 tot = sum(math.exp(s - m) for s in S[i])
                 out["lse"][b, h, i] = m + math.log(tot)
                 for j in range(N):
                     P[i][j] = math.exp(S[i][j] - m) / tot
                 for j in range(N):
-                    out["o"][b, h, i] += P[i][j] * v[j]
+                    out["o"][b, h, i] += P[i][j] * X[i][j] * v[j]
             o = out["o"][b, h]
             for i in range(N):
                 Di = dot(do[i], o[i])
                 for j in range(N):
                     if P[i][j] == 0.0:
                         continue
-                    out["dv"][b, h, j] += P[i][j] * do[i]
-                    dS = P[i][j] * (dot(do[i], v[j]) - Di)
+                    out["dv"][b, h, j] += P[i][j] * X[i][j] * do[i]
+                    dS = P[i][j] * (X[i][j] * dot(do[i], v[j]) - Di)
                     g = tau * dS
                     # d/dq_i and d/dk_j of the content term (q_i + u) . k_j
                     out["dq"][b, h, i] += g * k[j]
