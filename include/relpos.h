@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 2
+#define RELPOS_ABI_VERSION 3
 
 /* ---- return codes ---------------------------------------------------- */
 #define RELPOS_OK 0
@@ -120,17 +120,38 @@ typedef struct relpos_desc {
   int64_t aq_row_stride, aq_head_stride;
   int64_t ak_row_stride, ak_head_stride;
   int64_t bias_row_stride, bias_head_stride;
+  /* Segment mask ([RPA] appendix "Masks, packing, and dropout": padding
+     masks and packed variable-length sequences).  1: relpos_tensors.seg
+     holds, for every token t of batch row b, the bounds [start, end) of
+     its segment (int32 [B, N, 2], device memory, 8-byte aligned); a pair
+     (i, j) is visible iff j lies in i's segment.  Every token of a segment
+     must carry that segment's bounds; a padding token carries an empty
+     segment (start = end).  One segment [0, L) per row is a padding mask of
+     length L, several are packed sequences (offsets stay i - j).  A query
+     with no visible key gets O = 0, L = -inf and zero gradients. */
+  int32_t segmented;
+  /* Attention dropout: a pair is dropped with probability dropout_p8 / 256
+     (0..255; 0 = none) and kept probabilities are scaled by
+     256 / (256 - dropout_p8).  The mask comes from Philox4x32-10 (Salmon
+     et al., SC 2011) keyed by dropout_seed: counter (j >> 2, i >> 2,
+     b H + h, 0), byte (j & 3) of word (i & 3), kept iff >= dropout_p8.  The
+     backward regenerates the forward's mask from the same seed, so pass the
+     same descriptor to both.  The seed is not part of the cached plan. */
+  int32_t dropout_p8;
+  uint64_t dropout_seed;
 } relpos_desc;
 
 typedef struct relpos_shape {
   int32_t B, H, N, d;
 } relpos_shape;
 
-/* Device pointers; unused terms may be NULL.  u and v are [H, 64]. */
+/* Device pointers; unused terms may be NULL.  u and v are [H, 64].  seg:
+   int32 [B, N, 2] segment bounds, read when desc->segmented (else NULL). */
 typedef struct relpos_tensors {
   const void *q, *k, *v;
   const void *aq, *ak, *bias;
   const void *u, *vbias;
+  const int32_t *seg;
 } relpos_tensors;
 
 /* Device pointers.  dq/dk/dv in out_dtype; table gradients fp32 with the

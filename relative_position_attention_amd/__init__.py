@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     attn_bwd,
     empty_grads,
     set_stage_events,
+    segment_bounds,
     strerror,
     EXPORTED_SYMBOLS,
 )

@@ -12,7 +12,7 @@ EXPORTED_SYMBOLS = (
     "relpos_set_stage_events", "relpos_project_noalloc",
 )
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAP_KIND = {"identity": 0, "clipped": 1, "t5": 2, "log": 3, "explicit": 4}
 DTYPE = {"f32": 0, "bf16": 1}
 TERM = {"aq": 1, "ak": 2, "bias": 4, "u": 8, "v": 16}
@@ -41,7 +41,9 @@ class _Desc(ctypes.Structure):
                 ("split_operands", ctypes.c_int32), ("map", _Map),
                 ("aq_row_stride", ctypes.c_int64), ("aq_head_stride", ctypes.c_int64),
                 ("ak_row_stride", ctypes.c_int64), ("ak_head_stride", ctypes.c_int64),
-                ("bias_row_stride", ctypes.c_int64), ("bias_head_stride", ctypes.c_int64)]
+                ("bias_row_stride", ctypes.c_int64), ("bias_head_stride", ctypes.c_int64),
+                ("segmented", ctypes.c_int32), ("dropout_p8", ctypes.c_int32),
+                ("dropout_seed", ctypes.c_uint64)]
 
 
 class _Shape(ctypes.Structure):
@@ -50,7 +52,8 @@ class _Shape(ctypes.Structure):
 
 
 class _Tensors(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "aq", "ak", "bias", "u", "vbias")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k", "v", "aq", "ak", "bias", "u", "vbias",
+                                                "seg")]
 
 
 class _Grads(ctypes.Structure):
@@ -127,7 +130,10 @@ class Problem:
     """Descriptor and shape of one attention problem.
 
     ``spec`` uses the keys of the synthetic-problem recipes: B, H, N, d,
-    dtype, causal, scale, map, signs, terms, rows, aq_shared.  ``out_dtype``
+    dtype, causal, scale, map, signs, terms, rows, aq_shared, and optionally
+    segments (per batch row a list of token intervals [start, end); the
+    tensors then carry "seg", see segment_bounds) and dropout
+    ({"p8": drop probability in 1/256, "seed": 64-bit Philox key}).  ``out_dtype``
     is the dtype of O, dQ, dK, dV ("f32" or "bf16").  ``split_operands``
     sets the descriptor field of that name (bf16 inputs only): P and the
     score gradient enter their MFMA products as bf16 hi + lo pairs, which a
@@ -150,6 +156,11 @@ class Problem:
         d.sign_k = int(signs.get("ak", 1))
         d.sign_b = int(signs.get("bias", 1))
         d.split_operands = int(bool(split_operands))
+        d.segmented = int(spec.get("segments") is not None)
+        dr = spec.get("dropout")
+        if dr is not None:
+            d.dropout_p8 = int(dr["p8"])
+            d.dropout_seed = int(dr["seed"]) & 0xFFFFFFFFFFFFFFFF
         mp = spec["map"]
         d.map.kind = MAP_KIND[mp["kind"]]
         d.map.clip = int(mp.get("clip", 0))
@@ -197,6 +208,21 @@ def plan_rows(problem, which):
     return list(buf[:n])
 
 
+def segment_bounds(segments, B, N):
+    """The descriptor's segment-bound layout (int32 [B, N, 2]) of per-row
+    segment lists: token t of a segment [start, end) carries (start, end),
+    a token in no segment (padding) carries the empty (0, 0)."""
+    import numpy as np
+    out = np.zeros((B, N, 2), dtype=np.int32)
+    for b in range(B):
+        for start, end in segments[b]:
+            if not (0 <= start <= end <= N):
+                raise ValueError(f"segment ({start}, {end}) outside [0, {N}]")
+            out[b, start:end, 0] = start
+            out[b, start:end, 1] = end
+    return out
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -222,6 +248,11 @@ def _tensors(problem, t):
         ts.u = t["u"].data_ptr()
     if "v" in spec["terms"]:
         ts.vbias = t["v_bias"].data_ptr()
+    if spec.get("segments") is not None:
+        seg = t["seg"]
+        if not seg.is_cuda or not seg.is_contiguous():
+            raise ValueError("tensor seg must be a contiguous device tensor")
+        ts.seg = seg.data_ptr()
     return ts
 
 

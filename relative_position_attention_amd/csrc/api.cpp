@@ -91,6 +91,8 @@ std::string plan_key(const relpos_desc* d, const relpos_shape* sh) {
   put(key, d->ak_head_stride);
   put(key, d->bias_row_stride);
   put(key, d->bias_head_stride);
+  put(key, d->segmented);
+  put(key, d->dropout_p8);  // (the seed is read per call, not planned)
   if (m.kind == RELPOS_MAP_EXPLICIT && m.explicit_rows != nullptr && m.clip >= 0)
     key.append(reinterpret_cast<const char*>(m.explicit_rows),
                sizeof(int32_t) * (2 * static_cast<size_t>(m.clip) + 1));
@@ -185,6 +187,9 @@ int check_inputs(const Plan& p, const relpos_tensors* in) {
   if (p.bias && !in->bias) return fail(RELPOS_E_INVALID_ARG, "bias missing");
   if (p.u && !in->u) return fail(RELPOS_E_INVALID_ARG, "u missing");
   if (p.v && !in->vbias) return fail(RELPOS_E_INVALID_ARG, "v missing");
+  if (p.segmented && (in->seg == nullptr || (reinterpret_cast<uintptr_t>(in->seg) & 7)))
+    return fail(in->seg ? RELPOS_E_MISALIGNED : RELPOS_E_INVALID_ARG,
+                "segment bounds missing or not 8-byte aligned");
   return RELPOS_OK;
 }
 
@@ -413,11 +418,15 @@ AttnArgs attn_args(const Plan& p, const relpos_tensors* in, void* z, void* ws) {
   a.scale = p.scale;
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.out_f32 = p.out_dtype == RELPOS_DTYPE_F32;
+  a.seg = p.segmented ? in->seg : nullptr;
+  a.drop_p8 = p.drop_p8;
+  a.drop_scale = 256.f / static_cast<float>(256 - p.drop_p8);
   return a;
 }
 
 int base_flags(const Plan& p) {
   int f = 0;
+  if (p.segmented || p.drop_p8 > 0) f |= F_EXT;
   if (p.aq) f |= F_ZQ;
   if (p.ak) f |= F_ZK;
   if (p.bias && !p.aq) f |= F_BT;
@@ -519,6 +528,8 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   AttnArgs a = attn_args(p, in, z, ws);
   a.o = o;
   a.lse = lse;
+  a.seed_lo = static_cast<uint32_t>(desc->dropout_seed);
+  a.seed_hi = static_cast<uint32_t>(desc->dropout_seed >> 32);
   const int ff = base_flags(p) | (p.split ? F_SPLIT : 0);
   RP_MARK(0);
   if (p.dtype == RELPOS_DTYPE_F32)
@@ -578,6 +589,8 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   RP_MARK(1);
 
   AttnArgs a = attn_args(p, in, z, ws);
+  a.seed_lo = static_cast<uint32_t>(desc->dropout_seed);
+  a.seed_hi = static_cast<uint32_t>(desc->dropout_seed >> 32);
   a.dout = dout;
   a.o = const_cast<void*>(o);
   a.lse = const_cast<float*>(lse);
@@ -599,6 +612,13 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (q_direct) a.dqacc = static_cast<float*>(gr->dq);
   if (k_direct) a.dkacc = static_cast<float*>(gr->dk);
   const int bf = base_flags(p) | (p.split ? F_SPLIT : 0);
+
+  // With a segment mask the passes skip the tiles outside every segment of a
+  // workgroup, leaving those pairs' offset-gradient entries unwritten; the
+  // reductions read every entry a token's offsets reach, so the buffer is
+  // cleared before each pass (a fill kernel; the passes write the rest)
+  const size_t dz_bytes = static_cast<size_t>(p.BH) * a.dz_bh * p.dz_entry;
+  if (p.segmented && (p.need_qside || p.ak)) RP_HIP(launch_zero(dz, dz_bytes, s));
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
   const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0) |
@@ -702,6 +722,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   }
 
   // Key-parallel pass, then the key reduction
+  if (p.segmented && p.ak) RP_HIP(launch_zero(dz, dz_bytes, s));
   const int kflags = bf | (p.ak ? F_DZK : 0) | (p.u ? F_U : 0);
   RP_MARK(3);
   if (dt == 0)

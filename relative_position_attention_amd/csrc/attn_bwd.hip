@@ -1,6 +1,8 @@
 // Backward attention passes for fp32 inputs ([RPA] Table 9 "Query-parallel
 // pass" and "Key-parallel pass", Algorithm 2; bf16 inputs run bwd_q_fast.hip
-// and bwd_k_fast.hip).  [RPA] = "Fast and Exact Relative-
+// and bwd_k_fast.hip).
+// F_EXT adds segment masks (tested on every pair) and dropout
+// (G = tau P (dP keep - D), dV takes P keep), as defined in extras.hpp.  [RPA] = "Fast and Exact Relative-
 // Position Attention via Structure-Aware Kernels" (arXiv 2611.01182).
 //
 // Both passes rebuild each score tile from the saved logsumexp L and
@@ -17,6 +19,7 @@
 //    and (Transformer-XL u term) the key column sums of G.
 // No atomics anywhere: every output element has one writer and a fixed
 // summation order, so the results are bitwise reproducible.
+#include "extras.hpp"
 #include "relation.hpp"
 #include "tiles.hpp"
 
@@ -40,6 +43,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZQ) != 0;
+  constexpr bool EXT = (F & F_EXT) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][3][64 * P];  // K rows, K^T, V rows
 
   const int tid = threadIdx.x;
@@ -72,10 +76,22 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
     rlo[qb] = ok ? a.rowlo[tok + i] : 0.f;
     rhi[qb] = ok ? a.rowhi[tok + i] : 0.f;
     l2[qb] = ok ? a.lse[tok + i] * kLog2e : INFINITY;  // P = 0 on padding rows
+    if (EXT && !(l2[qb] > -INFINITY)) l2[qb] = INFINITY;  // a row with no key
     dd[qb] = ok ? a.dvec[tok + i] : 0.f;
   }
   GroupInfo giq = {0, 0, 0, 0};
   if ((F & F_ZQ) || DZ) giq = a.gq[i0 / kGroup];
+  const bool SEG = EXT && a.seg != nullptr;
+  const bool DROP = EXT && a.drop_p8 > 0;
+  int sgl[2] = {0, 0}, sgh[2] = {0, 0};
+  if (SEG) {
+    const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int i = iw + 16 * qb + c16;
+      if (i < N) token_segment(a, brow, i, sgl[qb], sgh[qb]);
+    }
+  }
 
   const int nkt = CAUSAL ? (ilast / 64 + 1) : (N + 63) / 64;
   int n_hi = (i0 - D - 63 >= 0) ? (i0 - D - 63) / 64 + 1 : 0;
@@ -136,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
     GroupInfo gik = {0, 0, 0, 0};
     const int gk0 = (j0 / kGroup) * kGroup;
     if (F & F_ZK) gik = a.gk[j0 / kGroup];
-    const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw);
+    const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw) || SEG;
     const int region = kt < n_hi ? SAT_HI : (kt < t_lo ? BAND : SAT_LO);
     float gv[2][4][4];
 #pragma unroll
@@ -152,15 +168,19 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
           relation_qrow<T, F, BAND>(a, tok, h, i, rlo[qb], rhi[qb], giq, gik, gk0, j1, acc);
         else
           relation_qrow<T, F, SAT_LO>(a, tok, h, i, rlo[qb], rhi[qb], giq, gik, gk0, j1, acc);
+        // dropout: dP of a dropped pair is 0, of a kept one times the scale
+        float mk[4] = {1.f, 1.f, 1.f, 1.f};
+        if (DROP) keep_row4(a, bh, i, j1, a.drop_scale, mk);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           float xv = acc[t] * a.scale_log2;
           if (need_mask) {
             const int j = j1 + t;
-            if (j >= N || (CAUSAL && j > i)) xv = -INFINITY;
+            if (j >= N || (CAUSAL && j > i) || (SEG && (j < sgl[qb] || j >= sgh[qb])))
+              xv = -INFINITY;
           }
           const float p = fast_exp2(xv - l2[qb]);
-          gv[qb][kb][t] = a.scale * p * (dp[qb][kb][t] - dd[qb]);
+          gv[qb][kb][t] = a.scale * p * (dp[qb][kb][t] * mk[t] - dd[qb]);
         }
         if (DZ) {
           if (region == SAT_HI) {
@@ -253,6 +273,7 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
+  constexpr bool EXT = (F & F_EXT) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * P];  // Q rows, Q^T, dO rows, dO^T
 
   const int tid = threadIdx.x;
@@ -286,6 +307,17 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   }
   GroupInfo gik = {0, 0, 0, 0};
   if ((F & F_ZK) || DZ) gik = a.gk[j0b / kGroup];
+  const bool SEG = EXT && a.seg != nullptr;
+  const bool DROP = EXT && a.drop_p8 > 0;
+  int sgl[2] = {0, 0}, sgh[2] = {0, 0};
+  if (SEG) {
+    const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int j = jw + 16 * kb + c16;
+      if (j < N) token_segment(a, brow, j, sgl[kb], sgh[kb]);
+    }
+  }
 
   // query tiles, ascending: saturated-low, band, saturated-high
   const int nqt = (N + 63) / 64;
@@ -355,7 +387,7 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
     GroupInfo giq = {0, 0, 0, 0};
     const int gq0 = (i0 / kGroup) * kGroup;
     if (F & F_ZQ) giq = a.gq[i0 / kGroup];
-    const bool need_mask = (i0 + 64 > N) || (j0b + 128 > N) || (CAUSAL && i0 < jw + 31);
+    const bool need_mask = (i0 + 64 > N) || (j0b + 128 > N) || (CAUSAL && i0 < jw + 31) || SEG;
     const int region = it < n_lo ? SAT_LO : (it < t_hi ? BAND : SAT_HI);
     float pv[2][4][4], gv[2][4][4];  // [kb][qb][t]
 #pragma unroll
@@ -368,6 +400,10 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
       load4_guard(a.rowhi + tok, i1, N, rh);
 #pragma unroll
       for (int t = 0; t < 4; ++t) l2[t] = (i1 + t < N) ? l2[t] * kLog2e : INFINITY;
+      if (EXT) {  // a row with no key (L = -inf): P = 0
+#pragma unroll
+        for (int t = 0; t < 4; ++t) l2[t] = l2[t] > -INFINITY ? l2[t] : INFINITY;
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int j = jw + 16 * kb + c16;
@@ -381,16 +417,20 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
         else
           relation_krow<T, F, SAT_LO>(a, tok, h, j, klo[kb], khi[kb], kmid[kb], rl, rh, giq, gq0,
                                       gik, i1, acc);
+        // dropout: G = tau P (dP keep - D), and dV takes P keep
+        float mk[4] = {1.f, 1.f, 1.f, 1.f};
+        if (DROP) keep_col4(a, bh, i1, j, a.drop_scale, mk);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           float xv = acc[t] * a.scale_log2;
           if (need_mask) {
             const int i = i1 + t;
-            if (j >= N || i >= N || (CAUSAL && j > i)) xv = -INFINITY;
+            if (j >= N || i >= N || (CAUSAL && j > i) || (SEG && (i < sgl[kb] || i >= sgh[kb])))
+              xv = -INFINITY;
           }
           const float p = fast_exp2(xv - l2[t]);
-          pv[kb][qb][t] = p;
-          gv[kb][qb][t] = a.scale * p * (dp[qb][kb][t] - dd[t]);
+          pv[kb][qb][t] = p * mk[t];
+          gv[kb][qb][t] = a.scale * p * (dp[qb][kb][t] * mk[t] - dd[t]);
         }
         if (CS) csum[kb] += gv[kb][qb][0] + gv[kb][qb][1] + gv[kb][qb][2] + gv[kb][qb][3];
         if (DZ) {
@@ -505,15 +545,15 @@ hipError_t launch_k(const AttnArgs& a, int B, hipStream_t s) {
   X(F_ZQ | F_DZQ | F_DZ32) X(F_BT | F_DZQ | F_DZ32) X(F_ZQ | F_ZK | F_DZQ | F_DZ32) \
   X(F_ZK | F_BT | F_DZQ | F_DZ32)
 
-template <typename T>
+template <typename T, int EXTF>
 hipError_t dispatch_q(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZQ | F_DZ32);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \
-    return launch_q<T, (X)>(a, B, s);          \
+    return launch_q<T, (X) | EXTF>(a, B, s);          \
   case (X) | F_CAUSAL:                               \
-    return launch_q<T, (X) | F_CAUSAL>(a, B, s);
+    return launch_q<T, (X) | F_CAUSAL | EXTF>(a, B, s);
     RP_QFLAGS(RP_CASE)
 #undef RP_CASE
     default:
@@ -526,15 +566,15 @@ hipError_t dispatch_q(int flags, const AttnArgs& a, int B, hipStream_t s) {
   X(F_U) X(F_ZQ | F_U) X(F_BT | F_U) X(F_ZQ | F_ZK | F_DZK | F_U) X(F_ZK | F_DZK | F_U) \
   X(F_ZK | F_BT | F_DZK | F_U)
 
-template <typename T>
+template <typename T, int EXTF>
 hipError_t dispatch_k(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL | F_DZK | F_U);
   switch (f) {
 #define RP_CASE(X)                                   \
   case X:                                            \
-    return launch_k<T, (X)>(a, B, s);          \
+    return launch_k<T, (X) | EXTF>(a, B, s);          \
   case (X) | F_CAUSAL:                               \
-    return launch_k<T, (X) | F_CAUSAL>(a, B, s);
+    return launch_k<T, (X) | F_CAUSAL | EXTF>(a, B, s);
     RP_KFLAGS(RP_CASE)
 #undef RP_CASE
     default:
@@ -545,11 +585,13 @@ hipError_t dispatch_k(int flags, const AttnArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_bwd_q_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  return dispatch_q<float>(flags, a, B, s);
+  if (flags & F_EXT) return dispatch_q<float, F_EXT>(flags, a, B, s);
+  return dispatch_q<float, 0>(flags, a, B, s);
 }
 
 hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  return dispatch_k<float>(flags, a, B, s);
+  if (flags & F_EXT) return dispatch_k<float, F_EXT>(flags, a, B, s);
+  return dispatch_k<float, 0>(flags, a, B, s);
 }
 
 }  // namespace relpos

@@ -16,7 +16,9 @@
 // The key loop is split into its three ranges (saturated-high, band,
 // saturated-low) once per workgroup from the tile's extreme offsets
 // ([RPA] §4.3.3: the ranges are fixed before the loop instead of testing
-// every tile).
+// every tile).  F_EXT adds segment masks (tested on every pair) and dropout
+// (P V takes P times the pair's keep factor), as defined in extras.hpp.
+#include "extras.hpp"
 #include "relation.hpp"
 #include "tiles.hpp"
 
@@ -33,6 +35,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NST = 64 / KS;
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
+  constexpr bool EXT = (F & F_EXT) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][2][64 * P];
 
   const int tid = threadIdx.x;
@@ -63,6 +66,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   }
   GroupInfo giq = {0, 0, 0, 0};
   if (F & F_ZQ) giq = a.gq[i0 / kGroup];
+  const bool SEG = EXT && a.seg != nullptr;
+  const bool DROP = EXT && a.drop_p8 > 0;
+  int sgl[2] = {0, 0}, sgh[2] = {0, 0};
+  if (SEG) {
+    const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int i = iw + 16 * qb + c16;
+      if (i < N) token_segment(a, brow, i, sgl[qb], sgh[qb]);
+    }
+  }
 
   // key-tile ranges from the workgroup's extreme offsets
   const int nkt = CAUSAL ? (ilast / 64 + 1) : (N + 63) / 64;
@@ -116,7 +130,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     GroupInfo gik = {0, 0, 0, 0};
     const int gk0 = (j0 / kGroup) * kGroup;
     if (F & F_ZK) gik = a.gk[j0 / kGroup];
-    const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw);
+    const bool need_mask = (j0 + 64 > N) || (CAUSAL && j0 + 63 > iw) || SEG;
     float x[2][4][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -136,7 +150,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
           float xv = acc[t] * a.scale_log2;
           if (need_mask) {
             const int j = j1 + t;
-            if (j >= N || (CAUSAL && j > i)) xv = -INFINITY;
+            if (j >= N || (CAUSAL && j > i) || (SEG && (j < sgl[qb] || j >= sgh[qb])))
+              xv = -INFINITY;
           }
           x[qb][kb][t] = xv;
         }
@@ -169,6 +184,18 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
     }
+    if (DROP) {
+      // P V takes the dropped probabilities (the row sums above keep P)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float mk[4];
+          keep_row4(a, bh, iw + 16 * qb + c16, j0 + 16 * kb + 4 * g, a.drop_scale, mk);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[qb][kb][t] *= mk[t];
+        }
+    }
 
     // O^T += V^T P^T
 #pragma unroll
@@ -196,14 +223,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     const float ls = wave_sum_g(l[qb]);
     const int i = iw + 16 * qb + c16;
     if (i >= N) continue;
-    const float inv = 1.f / ls;
+    // (a query whose segment is empty has no key: O = 0, L = -inf)
+    const float inv = (EXT && !(ls > 0.f)) ? 0.f : 1.f / ls;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       float vals[4] = {o[qb][db][0] * inv, o[qb][db][1] * inv, o[qb][db][2] * inv,
                        o[qb][db][3] * inv};
       store_out4(a.o, (tok + i) * 64 + 16 * db + 4 * g, a.out_f32 != 0, vals);
     }
-    if (g == 0) a.lse[tok + i] = m[qb] * kLn2 + logf(ls);
+    if (g == 0) a.lse[tok + i] = (EXT && !(ls > 0.f)) ? -INFINITY : m[qb] * kLn2 + logf(ls);
   }
 }
 
@@ -214,13 +242,13 @@ hipError_t launch_one(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int EXTF>
 hipError_t dispatch(int flags, const AttnArgs& a, int B, hipStream_t s) {
   const int f = flags & (F_ZQ | F_ZK | F_BT | F_CAUSAL);
   switch (f) {
 #define RP_CASE(X) \
   case X:          \
-    return launch_one<T, (X)>(a, B, s);
+    return launch_one<T, (X) | EXTF>(a, B, s);
     RP_CASE(0)
     RP_CASE(F_ZQ)
     RP_CASE(F_ZK)
@@ -242,7 +270,8 @@ hipError_t dispatch(int flags, const AttnArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  return dispatch<float>(flags, a, B, s);
+  if (flags & F_EXT) return dispatch<float, F_EXT>(flags, a, B, s);
+  return dispatch<float, 0>(flags, a, B, s);
 }
 
 }  // namespace relpos

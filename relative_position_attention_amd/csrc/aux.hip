@@ -765,6 +765,20 @@ hipError_t launch_fold_meta(const int32_t* beta, int32_t* fold, int S, int R, hi
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; k < n16; k += stride)
+    p[k] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(nblk(n16, 256), 4096));
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_expand(int dtype, const ExpandArgs& e, hipStream_t s) {
   const int vec = dtype == 0 ? 4 : 8;
   const int64_t total = static_cast<int64_t>(e.Ht) * e.S * (64 / vec);

@@ -24,6 +24,7 @@ enum : int {
   F_SPLIT = 128,  // bf16: P and G enter their MFMA products as bf16 hi + lo
   F_DZ32 = 256,   // backward: query-side offset gradients stored in fp32
   F_DZ16 = 512,   // backward: query-side offset gradients stored in fp16
+  F_EXT = 1024,   // segment masks and / or attention dropout (extras.hpp)
 };
 
 struct AttnArgs {
@@ -57,6 +58,12 @@ struct AttnArgs {
   float scale;       // tau
   float scale_log2;  // tau * log2(e)
   int out_f32;
+  // F_EXT kernels: segment bounds [B, N, 2] (null: no segment mask) and the
+  // dropout byte threshold p8 (0: no dropout), keep scale and Philox key
+  const int32_t* seg;
+  int drop_p8;
+  float drop_scale;
+  uint32_t seed_lo, seed_hi;
 };
 
 // Each launcher returns the hipError_t of its launch.
@@ -70,6 +77,11 @@ hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_
 // reads (bwd_q_fast.hip, bwd_k_fast.hip)
 hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
+// the F_EXT variants of the three bf16 kernels (fwd_ext.hip, bwd_q_ext.hip,
+// bwd_k_ext.hip); the launchers above forward F_EXT calls to them
+hipError_t launch_attn_fwd_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_q_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_k_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
 
 // ---- auxiliary kernels (aux.hip)
 
@@ -155,6 +167,9 @@ struct RowKeyArgs {
   int N, H, S;
 };
 hipError_t launch_rowkey(int dtype, const RowKeyArgs& a, int BH, hipStream_t s);
+
+// Zeroes `bytes` bytes at p (16-byte aligned; bytes a multiple of 16).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_rowdot(int dtype, int out_f32, const void* o, const void* dout, float* dvec,
                          int64_t rows, hipStream_t s);

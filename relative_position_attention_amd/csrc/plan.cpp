@@ -305,6 +305,14 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     detail = "split_operands must be 0 or 1";
     return RELPOS_E_INVALID_ARG;
   }
+  if (desc->segmented != 0 && desc->segmented != 1) {
+    detail = "segmented must be 0 or 1";
+    return RELPOS_E_INVALID_ARG;
+  }
+  if (desc->dropout_p8 < 0 || desc->dropout_p8 > 255) {
+    detail = "dropout_p8 must be in 0..255";
+    return RELPOS_E_INVALID_ARG;
+  }
   if (!std::isfinite(desc->scale) || !(desc->scale > 0.f)) {
     detail = "scale must be finite and positive";
     return RELPOS_E_INVALID_ARG;
@@ -337,6 +345,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.dzq_f32 = p.bias || (p.v && f32in);
   p.dzq_f16 = p.v && !p.bias && !f32in;
   p.split = desc->split_operands != 0 && p.dtype == RELPOS_DTYPE_BF16;
+  p.segmented = desc->segmented != 0;
+  p.drop_p8 = desc->dropout_p8;
   bool any_table = p.aq || p.ak || p.bias;
   if (any_table && p.R < 1) {
     detail = "num_rows must be >= 1";

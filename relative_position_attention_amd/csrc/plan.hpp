@@ -47,6 +47,8 @@ struct Plan {
   bool dzq_f16 = false;    // query-side offset gradients in fp16 (v without a bias)
   size_t dz_entry = 2;     // bytes per entry of the shared offset-gradient buffer
   bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
+  bool segmented = false;  // segment mask (tensors->seg)
+  int drop_p8 = 0;         // dropout probability in units of 1/256
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
   // Per table (A^Q, A^K, b): rows that are not one interval of expanded rows
   // fold through an index list (fold_rows: [R, 2] first / last position of

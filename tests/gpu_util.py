@@ -18,6 +18,9 @@ def to_device(spec, arrays):
     for name, arr in arrays.items():
         # values are exactly representable in dt: the conversion is exact
         out[name] = torch.from_numpy(np.ascontiguousarray(arr)).to(dt).cuda()
+    if spec.get("segments") is not None:
+        out["seg"] = torch.from_numpy(rpa.segment_bounds(spec["segments"], spec["B"],
+                                                         spec["N"])).cuda()
     return out
 
 
