@@ -213,6 +213,135 @@ def peak_memory(run, torch, rpa, out_dtype):
     return fwd, bwd
 
 
+def visible_pairs(spec):
+    """Visible (query, key) pairs of one (batch, head) slice, summed over the
+    batch rows: N^2 (causal: N (N + 1) / 2) without segments, else the sum
+    over segments of len^2 (causal: len (len + 1) / 2)."""
+    N = spec["N"]
+    segs = spec.get("segments")
+    if segs is None:
+        return spec["B"] * (N * (N + 1) / 2.0 if spec["causal"] else float(N) * N)
+    tot = 0.0
+    for row in segs:
+        for s0, s1 in row:
+            n = s1 - s0
+            tot += n * (n + 1) / 2.0 if spec["causal"] else float(n) * n
+    return tot
+
+
+def time_variant(label, spec, arr, torch, rpa, split, steps, warmup, flush, retain=True):
+    """Forward (projection + attention, or attention alone recomputing the
+    projections) and backward of one problem variant, median ms over `steps`
+    flushed samples, with credited TFLOP/s over its visible pairs and the
+    peak MiB beyond the inputs of each pass."""
+    dt = torch.bfloat16
+    t = {k: torch.from_numpy(v).to(dt).cuda() for k, v in arr.items()}
+    if spec.get("segments") is not None:
+        t["seg"] = torch.from_numpy(rpa.segment_bounds(spec["segments"], spec["B"],
+                                                       spec["N"])).cuda()
+    prob = rpa.Problem(spec, out_dtype="f32", split_operands=split)
+    B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
+    pairs = visible_pairs(spec) * H
+    nproj = sum(1 for x in ("aq", "ak") if x in spec["terms"])
+    fwd_flops = 4.0 * pairs * d + nproj * 2.0 * B * H * N * spec.get("rows", 0) * d
+    sz = rpa.plan_sizes(prob)
+    z = torch.empty(max(sz["z_bytes"], 256), dtype=torch.uint8, device="cuda") if retain else None
+    ws_f = torch.empty(max(sz["fwd_ws_bytes"] if retain else sz["fwd_ws_bytes_noz"], 256),
+                       dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(max(sz["bwd_ws_bytes"] if retain else sz["bwd_ws_bytes_noz"], 256),
+                       dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H, N, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    grads = rpa.empty_grads(prob, torch.device("cuda"))
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        if retain:
+            rpa.project(prob, t, z=z, ws=ws_f)
+            rpa.attn_fwd(prob, t, z=z, o=o, lse=lse)
+        else:
+            rpa.attn_fwd(prob, t, z=None, retain=False, o=o, lse=lse, ws=ws_f)
+
+    def bwd():
+        rpa.attn_bwd(prob, t, o, lse, t["do"], z=z, grads=grads, ws=ws_b)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e4 in ev:
+        flush.fill_(1.0)
+        e4[0].record(stream)
+        fwd()
+        e4[1].record(stream)
+        flush.fill_(2.0)
+        e4[2].record(stream)
+        bwd()
+        e4[3].record(stream)
+    torch.cuda.synchronize()
+
+    def med(xs):
+        xs = sorted(xs)
+        n = len(xs)
+        return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+    f_ms = med([e[0].elapsed_time(e[1]) for e in ev])
+    b_ms = med([e[2].elapsed_time(e[3]) for e in ev])
+    # peak memory beyond the inputs (the library allocates nothing itself)
+    torch.cuda.synchronize()
+    del z, ws_f, ws_b, o, lse, grads
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o2, l2, z2 = rpa.attn_fwd(prob, t, retain=retain)
+    torch.cuda.synchronize()
+    f_mib = (torch.cuda.max_memory_allocated() - base) / 2**20
+    base2 = torch.cuda.memory_allocated() - (z2.numel() if z2 is not None else 0)
+    torch.cuda.reset_peak_memory_stats()
+    g2 = rpa.attn_bwd(prob, t, o2, l2, t["do"], z=z2)
+    torch.cuda.synchronize()
+    b_mib = (torch.cuda.max_memory_allocated() - base2) / 2**20
+    del o2, l2, z2, g2, t
+    torch.cuda.empty_cache()
+    return {"variant": label, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "fwd_tflops": round(fwd_flops / f_ms / 1e9, 2),
+            "bwd_tflops": round(2 * fwd_flops / b_ms / 1e9, 2),
+            "fwd_peak_mib": round(f_mib, 1), "bwd_peak_mib": round(b_mib, 1)}
+
+
+def extras(torch, rpa, synth, flush, steps=5, warmup=2):
+    """The path's other modes at the 8K Shaw shape (B = 2, H = 12, clip 256):
+    the same call with retained projections as the reference row, packed
+    sequences (four documents of 2048 tokens per row, segment mask),
+    padding (row lengths 8192 and 5000), attention dropout (26/256), a map
+    whose rows are not contiguous offset intervals (|delta| clipped at 256,
+    delta and -delta sharing a row), and projections recomputed in both
+    passes instead of retained.  Credited FLOPs count visible pairs."""
+    import copy
+    spec0, arr0 = synth.make_bench("shaw")
+    out = []
+    out.append(time_variant("retained (reference)", spec0, arr0, torch, rpa, False, steps, warmup,
+                            flush))
+    packed = dict(spec0, segments=[[(k * 2048, (k + 1) * 2048) for k in range(4)]] * 2)
+    out.append(time_variant("packed 4 x 2048", packed, arr0, torch, rpa, False, steps, warmup,
+                            flush))
+    padded = dict(spec0, segments=[[(0, 8192)], [(0, 5000)]])
+    out.append(time_variant("padded 8192 / 5000", padded, arr0, torch, rpa, False, steps, warmup,
+                            flush))
+    drop = dict(spec0, dropout={"p8": 26, "seed": 12345})
+    out.append(time_variant("dropout 26/256", drop, arr0, torch, rpa, False, steps, warmup, flush))
+    sym = copy.deepcopy(spec0)
+    c = spec0["map"]["clip"]
+    sym["map"] = {"kind": "explicit", "clip": c, "rows": [abs(x) for x in range(-c, c + 1)]}
+    sym["rows"] = c + 1
+    arr_sym = dict(arr0, aq=arr0["aq"][: c + 1].copy())
+    out.append(time_variant("non-contiguous map |delta|", sym, arr_sym, torch, rpa, False, steps,
+                            warmup, flush))
+    out.append(time_variant("recomputed projections", spec0, arr0, torch, rpa, False, steps,
+                            warmup, flush, retain=False))
+    return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as fh:
@@ -307,6 +436,7 @@ def main():
     ap.add_argument("--mechs", default=",".join(MECHS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this library has no "
@@ -504,6 +634,11 @@ def main():
         "roofline": roofline,
         "hbm": hbm,
     }
+    if not args.no_extras:
+        del runs
+        torch.cuda.empty_cache()
+        out["extras"] = extras(torch, rpa, synth, flush)
+        runs = None
     if not args.no_cpu_baseline:
         del runs
         torch.cuda.empty_cache()

@@ -426,7 +426,8 @@ AttnArgs attn_args(const Plan& p, const relpos_tensors* in, void* z, void* ws) {
 
 int base_flags(const Plan& p) {
   int f = 0;
-  if (p.segmented || p.drop_p8 > 0) f |= F_EXT;
+  if (p.segmented) f |= F_SEG;
+  if (p.drop_p8 > 0) f |= F_DROP;
   if (p.aq) f |= F_ZQ;
   if (p.ak) f |= F_ZK;
   if (p.bias && !p.aq) f |= F_BT;

@@ -1,7 +1,7 @@
 // Backward attention passes for fp32 inputs ([RPA] Table 9 "Query-parallel
 // pass" and "Key-parallel pass", Algorithm 2; bf16 inputs run bwd_q_fast.hip
 // and bwd_k_fast.hip).
-// F_EXT adds segment masks (tested on every pair) and dropout
+// F_SEG adds segment masks (tested on every pair), F_DROP dropout
 // (G = tau P (dP keep - D), dV takes P keep), as defined in extras.hpp.  [RPA] = "Fast and Exact Relative-
 // Position Attention via Structure-Aware Kernels" (arXiv 2611.01182).
 //
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZQ) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][3][64 * P];  // K rows, K^T, V rows
 
   const int tid = threadIdx.x;
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnArgs a) {
   }
   GroupInfo giq = {0, 0, 0, 0};
   if ((F & F_ZQ) || DZ) giq = a.gq[i0 / kGroup];
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   int sgl[2] = {0, 0}, sgh[2] = {0, 0};
   if (SEG) {
     const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][4][64 * P];  // Q rows, Q^T, dO rows, dO^T
 
   const int tid = threadIdx.x;
@@ -307,8 +307,8 @@ __global__ __launch_bounds__(256) void attn_bwd_k_kernel(AttnArgs a) {
   }
   GroupInfo gik = {0, 0, 0, 0};
   if ((F & F_ZK) || DZ) gik = a.gk[j0b / kGroup];
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   int sgl[2] = {0, 0}, sgh[2] = {0, 0};
   if (SEG) {
     const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
@@ -585,12 +585,12 @@ hipError_t dispatch_k(int flags, const AttnArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_bwd_q_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (flags & F_EXT) return dispatch_q<float, F_EXT>(flags, a, B, s);
+  if (flags & (F_SEG | F_DROP)) return dispatch_q<float, F_SEG | F_DROP>(flags, a, B, s);
   return dispatch_q<float, 0>(flags, a, B, s);
 }
 
 hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (flags & F_EXT) return dispatch_k<float, F_EXT>(flags, a, B, s);
+  if (flags & (F_SEG | F_DROP)) return dispatch_k<float, F_SEG | F_DROP>(flags, a, B, s);
   return dispatch_k<float, 0>(flags, a, B, s);
 }
 

@@ -16,7 +16,7 @@
 // The key loop is split into its three ranges (saturated-high, band,
 // saturated-low) once per workgroup from the tile's extreme offsets
 // ([RPA] §4.3.3: the ranges are fixed before the loop instead of testing
-// every tile).  F_EXT adds segment masks (tested on every pair) and dropout
+// every tile).  F_SEG adds segment masks (tested on every pair), F_DROP dropout
 // (P V takes P times the pair's keep factor), as defined in extras.hpp.
 #include "extras.hpp"
 #include "relation.hpp"
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NST = 64 / KS;
   constexpr int P = TileP<T>::P;
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   __shared__ __attribute__((aligned(16))) T lds[2][2][64 * P];
 
   const int tid = threadIdx.x;
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
   }
   GroupInfo giq = {0, 0, 0, 0};
   if (F & F_ZQ) giq = a.gq[i0 / kGroup];
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   int sgl[2] = {0, 0}, sgh[2] = {0, 0};
   if (SEG) {
     const int64_t brow = static_cast<int64_t>(bh / a.H) * N;
@@ -270,7 +270,8 @@ hipError_t dispatch(int flags, const AttnArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(int flags, const AttnArgs& a, int B, hipStream_t s) {
-  if (flags & F_EXT) return dispatch<float, F_EXT>(flags, a, B, s);
+  // (one variant takes both extras, each switched on at run time)
+  if (flags & (F_SEG | F_DROP)) return dispatch<float, F_SEG | F_DROP>(flags, a, B, s);
   return dispatch<float, 0>(flags, a, B, s);
 }
 

@@ -24,9 +24,10 @@
 // dZ~^K[j, delta + D] (single writer, aligned 4-entry runs); pairs with
 // |delta| >= D add into two fp32 per-key boundary sums; with the
 // Transformer-XL u term the column sums of G are kept too.  No atomics.
-// F_EXT adds segment masks (query tiles limited to the union of the
-// workgroup's keys' segments, per-pair tests elsewhere) and dropout
-// (G' = P (dP keep - D), dV takes P keep), as defined in extras.hpp.
+// F_SEG adds segment masks (query tiles limited to the union of the
+// workgroup's keys' segments, per-pair tests elsewhere), F_DROP dropout
+// (G' = P (dP keep - D), dV takes P keep; segments are then taken when
+// given), as defined in extras.hpp.
 #pragma once
 #include "extras.hpp"
 #include "relation.hpp"
@@ -43,7 +44,7 @@ template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int total, int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   // fp16 P in dV = P^T dO (under F_SPLIT): dO and V as fp16 words
   constexpr bool HP = SPLIT;
   constexpr bool DZ = (F & F_DZK) != 0;
@@ -170,8 +171,8 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 
   // segment masks: each key's segment (the queries that see it), the wave's
   // union and intersection, and the workgroup's query tiles [it_first, it_end)
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   // (defined on every path: the per-pair tests read them only when SEG)
   int sgl[2], sgh[2];
 #pragma unroll
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
         const floatx4 qdd = *reinterpret_cast<const floatx4*>(&sqs[buf][1][16 * qb + 4 * g]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if constexpr (EXT) {
+          if constexpr ((F & F_DROP) != 0) {
             // dropout: G' = P (dP keep scale - D), and dV takes P keep (0 or
             // 1; the keep scale multiplies the finished dV in fp32)
             float mk[4] = {1.f, 1.f, 1.f, 1.f};

@@ -17,9 +17,10 @@
 // dZ~^Q[i, delta + D] -- one entry per (query, offset), a single writer,
 // written as aligned 4-entry runs; pairs with |delta| >= D add into two fp32
 // per-query boundary sums kept on chip ("Local Boundary Sums").  No atomics.
-// F_EXT adds segment masks (key tiles limited to the union of the
-// workgroup's segments, per-pair tests elsewhere) and dropout (dP takes the
-// pair's keep factor: G' = P (dP keep - D)), as defined in extras.hpp.
+// F_SEG adds segment masks (key tiles limited to the union of the
+// workgroup's segments, per-pair tests elsewhere), F_DROP dropout (dP takes
+// the pair's keep factor: G' = P (dP keep - D); segments are then taken when
+// given), as defined in extras.hpp.
 #pragma once
 #include "extras.hpp"
 #include "relation.hpp"
@@ -35,7 +36,7 @@ template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int total, int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   constexpr bool HOISTQ = (F & F_ZQ) && !(F & F_ZK);
   constexpr bool DZ = (F & F_DZQ) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
@@ -175,8 +176,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 
   // segment masks: each query's segment, the wave's union and intersection,
   // and the workgroup's key tiles [kt_begin, kt_end)
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   // (defined on every path: the per-pair tests read them only when SEG)
   int sgl[2], sgh[2];
 #pragma unroll
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           if (DROP) keep_row4(a, bh, qbase[qb] + c16, j0 + 16 * kb + 4 * g, a.drop_scale, mk);
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            s[qb][kb][t] *= EXT ? fmaf(dp[qb][kb][t], mk[t], -dd[qb]) : dp[qb][kb][t] - dd[qb];
+            s[qb][kb][t] *= (F & F_DROP) ? fmaf(dp[qb][kb][t], mk[t], -dd[qb]) : dp[qb][kb][t] - dd[qb];
         }
       }
 

@@ -30,10 +30,11 @@
 //   (two under F_SPLIT, one per part).
 // The region of each tile is decided per wave from the wave's extreme offsets
 // before the loop (the three ranges of [RPA] §4.3.3).
-// F_EXT adds segment masks (the key-tile loop covers the union of the
+// F_SEG adds segment masks (the key-tile loop covers the union of the
 // workgroup's segments; per-pair tests on tiles not inside every query's
-// segment) and dropout (P V takes P times the pair's keep factor; the row
-// sums, hence L, keep P itself), as defined in extras.hpp.
+// segment), F_DROP dropout (P V takes P times the pair's 0/1 keep mask and O
+// the keep scale; the row sums, hence L, keep P itself; segments are then
+// taken when given), as defined in extras.hpp.
 #pragma once
 #include "extras.hpp"
 #include "relation.hpp"
@@ -52,11 +53,12 @@ constexpr float kLazy = 8.f;       // rescale threshold, log2 units
 #define kOnes8 (__builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}))
 
 template <int F>
-__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || (F & F_EXT)) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
+__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || (F & F_DROP) ||
+                                                  ((F & F_SEG) && (F & F_BT))) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
                                                           int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
-  constexpr bool EXT = (F & F_EXT) != 0;
+  constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   // per-key relation entries: with a key table (F_ZK) the band value and the
   // two boundary values differ per key; with only the Transformer-XL u term
   // they are one value u . k_j
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
   // segment masks: each query's segment, the wave's union and intersection,
   // and the workgroup's key tiles [kt_begin, kt_end) (those holding a key of
   // some query's segment)
-  const bool SEG = EXT && a.seg != nullptr;
-  const bool DROP = EXT && a.drop_p8 > 0;
+  const bool SEG = (F & F_SEG) != 0 && a.seg != nullptr;
+  const bool DROP = (F & F_DROP) != 0 && a.drop_p8 > 0;
   // (defined on every path: the per-pair tests read them only when SEG)
   int sgl[QB], sgh[QB];
 #pragma unroll
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
             const float x = s[qb][2 * c + (e >> 2)][e & 3];
             pf[qb][e] = static_cast<bf16>(x);
             if (SPLIT) pl[qb][e] = static_cast<bf16>(x - static_cast<float>(pf[qb][e]));
-            if (EXT) {
+            if constexpr ((F & F_DROP) != 0) {
               const float xd = x * mk[e >> 2][e & 3];
               pd[qb][e] = static_cast<bf16>(xd);
               if (SPLIT) pdl[qb][e] = static_cast<bf16>(xd - static_cast<float>(pd[qb][e]));
@@ -537,10 +539,10 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             if (qb == 0 && !act[0]) continue;
-            // (with F_EXT P V takes the dropped probabilities)
-            o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, EXT ? pd[qb] : pf[qb], o[qb][db], 0, 0, 0);
+            // (with F_DROP P V takes the dropped probabilities)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, (F & F_DROP) ? pd[qb] : pf[qb], o[qb][db], 0, 0, 0);
             if (SPLIT)
-              o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, EXT ? pdl[qb] : pl[qb], o[qb][db], 0, 0, 0);
+              o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, (F & F_DROP) ? pdl[qb] : pl[qb], o[qb][db], 0, 0, 0);
           }
         }
 #pragma unroll

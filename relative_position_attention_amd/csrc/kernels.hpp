@@ -24,7 +24,8 @@ enum : int {
   F_SPLIT = 128,  // bf16: P and G enter their MFMA products as bf16 hi + lo
   F_DZ32 = 256,   // backward: query-side offset gradients stored in fp32
   F_DZ16 = 512,   // backward: query-side offset gradients stored in fp16
-  F_EXT = 1024,   // segment masks and / or attention dropout (extras.hpp)
+  F_SEG = 1024,   // segment masks (extras.hpp)
+  F_DROP = 2048,  // attention dropout, with segment masks when given (extras.hpp)
 };
 
 struct AttnArgs {
@@ -58,7 +59,7 @@ struct AttnArgs {
   float scale;       // tau
   float scale_log2;  // tau * log2(e)
   int out_f32;
-  // F_EXT kernels: segment bounds [B, N, 2] (null: no segment mask) and the
+  // F_SEG / F_DROP kernels: segment bounds [B, N, 2] (null: no segment mask) and the
   // dropout byte threshold p8 (0: no dropout), keep scale and Philox key
   const int32_t* seg;
   int drop_p8;
@@ -77,11 +78,16 @@ hipError_t launch_attn_bwd_k_f32(int flags, const AttnArgs& a, int B, hipStream_
 // reads (bwd_q_fast.hip, bwd_k_fast.hip)
 hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16(int flags, const AttnArgs& a, int B, hipStream_t s);
-// the F_EXT variants of the three bf16 kernels (fwd_ext.hip, bwd_q_ext.hip,
-// bwd_k_ext.hip); the launchers above forward F_EXT calls to them
-hipError_t launch_attn_fwd_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
-hipError_t launch_bwd_q_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
-hipError_t launch_bwd_k_bf16_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
+// the segment-mask (F_SEG: fwd_seg.hip, bwd_q_seg.hip, bwd_k_seg.hip) and
+// dropout (F_DROP | F_SEG: fwd_drop.hip, bwd_q_drop.hip, bwd_k_drop.hip)
+// variants of the three bf16 kernels; the launchers above forward such
+// calls to them
+hipError_t launch_attn_fwd_bf16_seg(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_q_bf16_seg(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_k_bf16_seg(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_fwd_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_q_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_k_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
 
 // ---- auxiliary kernels (aux.hip)
 
