@@ -10,7 +10,8 @@ Timing follows the pages' appendix "Kernel benchmarks": a 512 MiB device
 write flushes the caches before every forward and every backward sample;
 each pass and kernel is reported as the median (with min and max) of the
 timed steps, measured with HIP events on the launch stream; GPU clocks,
-power and temperature are recorded (amd-smi) before and after.
+power and temperature are recorded: amd-smi before the GPU is touched, the
+GPU's sysfs hwmon files before and after the timed region.
 
 Useful FLOPs follow the credit of "Fast and Exact Relative-Position Attention
 via Structure-Aware Kernels" (§5.1 evaluation setup, throughput paragraph):
@@ -354,11 +355,13 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-def gpu_state():
-    """Clocks, power and temperature of GPU 0 as amd-smi reports them (the
-    pages record these instead of locking clocks): the numeric fields whose
-    names mention a clock, power or temperature, or the tool's error."""
+def smi_state():
+    """Clocks, power and temperature of GPU 0 as amd-smi reports them: the
+    numeric fields whose names mention a clock, power or temperature, or the
+    tool's error.  Runs amd-smi as a child process, so it is called only
+    before this process touches the GPU."""
     import subprocess
+    err = "not run"
     for cmd in (["amd-smi", "metric", "-g", "0", "-p", "-c", "-t", "--json"],
                 ["rocm-smi", "--showtemp", "--showpower", "--showclocks", "--json"]):
         try:
@@ -388,44 +391,61 @@ def gpu_state():
             else:
                 name = "/".join(path)
                 low = name.lower()
-                if any(t in low for t in ("clk", "clock", "power", "temp", "sclk", "mclk")):
+                if any(t in low for t in ("clk", "clock", "power", "temp")) and x != "N/A":
                     out[name] = x
         walk(data, [])
         return {"tool": cmd[0], "fields": out}
     return {"tool": None, "error": err}
 
 
-def cpu_baseline(mechs):
-    """The fp64 oracle on one (batch, head) slice of each mechanism's bench
-    shape, timed on the host; credited FLOPs of those slices per second."""
-    import numpy as np  # noqa: F401
-    import oracle
-    import synth
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    total_s, total_flops, rounds = 0.0, 0.0, 0
-    problems = {}
-    # whole rounds over the mechanisms until at least 10 s of oracle work
-    while rounds < 4 and (rounds == 0 or total_s < 10.0):
-        for name in mechs:
-            if name not in problems:
-                kw = dict(synth.BENCH_SHAPES[name])
-                problems[name] = synth.make_problem(**dict(kw, B=1, H=1))
-            spec, arr = problems[name]
-            t0 = time.perf_counter()
-            oracle.slice_forward_backward(spec, arr, 0, 0)
-            total_s += time.perf_counter() - t0
-            f, b = credited_flops(spec)
-            total_flops += f + b
-        rounds += 1
-    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
-            "sample": f"{rounds} x one (batch, head) slice of each of {','.join(mechs)} at N=8192, "
-                      f"fp64 forward+backward ({total_s:.1f} s)"}
+def sysfs_state():
+    """Current shader clock, power and temperatures of the first AMD GPU from
+    its sysfs hwmon files (plain file reads, so it runs while this process
+    holds the GPU)."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as fh:
+                if fh.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            for f in sorted(glob.glob(os.path.join(hw, "*_input")) +
+                            glob.glob(os.path.join(hw, "power*_average"))):
+                name = os.path.basename(f)
+                try:
+                    with open(f) as fh:
+                        val = int(fh.read().strip())
+                except (OSError, ValueError):
+                    continue
+                label = name
+                lf = f.replace("_input", "_label").replace("_average", "_label")
+                if os.path.exists(lf):
+                    try:
+                        with open(lf) as fh:
+                            label = fh.read().strip() + " (" + name + ")"
+                    except OSError:
+                        pass
+                if name.startswith("freq"):
+                    out[label] = f"{val / 1e6:.0f} MHz"
+                elif name.startswith("power"):
+                    out[label] = f"{val / 1e6:.1f} W"
+                elif name.startswith("temp"):
+                    out[label] = f"{val / 1e3:.1f} C"
+        sclk = os.path.join(dev, "pp_dpm_sclk")
+        if os.path.exists(sclk):
+            try:
+                with open(sclk) as fh:
+                    cur = [ln.strip() for ln in fh if "*" in ln]
+                if cur:
+                    out["pp_dpm_sclk"] = cur[0]
+            except OSError:
+                pass
+        if out:
+            return out
+    return {"error": "no readable AMD GPU hwmon files"}
 
 
 def main():
@@ -437,6 +457,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip amd-smi (e.g. under a profiler that preloads into child programs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this library has no "
@@ -444,6 +466,8 @@ def main():
               "the table gradients need one all-reduce",
               file=sys.stderr)
         sys.exit(2)
+    # amd-smi is a child program: read it before this process touches the GPU
+    smi = smi_state() if not args.no_gpu_state else {"tool": None, "error": "skipped"}
     import torch
 
     import relative_position_attention_amd as rpa
@@ -488,7 +512,7 @@ def main():
         for pe, fe, be in row:
             for e in pe + fe + be:
                 e.record(stream)
-    state_before = gpu_state()
+    state_before = sysfs_state()
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -509,7 +533,7 @@ def main():
             rpa.set_stage_events([])
     t_end.record(stream)
     torch.cuda.synchronize()
-    state_after = gpu_state()
+    state_after = sysfs_state()
     wall_ms = t_start.elapsed_time(t_end) / args.steps
 
     def stats(fn):
@@ -629,7 +653,8 @@ def main():
                                "forward and every backward sample",
                    "ms_per_step": "mean over the steps of the passes' own time (flushes "
                                   "excluded)", "wall_ms_per_step_with_flushes": round(wall_ms, 4)},
-        "gpu_state": {"before": state_before, "after": state_after},
+        "gpu_state": {"amd_smi_at_start": smi, "sysfs_before_timed": state_before,
+                      "sysfs_after_timed": state_after},
         "mechanisms": per,
         "roofline": roofline,
         "hbm": hbm,
