@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RELPOS_ABI_VERSION 3
+#define RELPOS_ABI_VERSION 4
 
 /* ---- return codes ---------------------------------------------------- */
 #define RELPOS_OK 0
@@ -139,6 +139,23 @@ typedef struct relpos_desc {
      same descriptor to both.  The seed is not part of the cached plan. */
   int32_t dropout_p8;
   uint64_t dropout_seed;
+  /* In-tile relation products ([RPA] §6 "Limitations" and Table 7, row
+     "Projections": the tiles compute their own relation products instead of
+     reading stored projections).  1: no projection Z^Q is stored; every
+     attention pass computes the products q_i . A~^Q[s] for the rows s its
+     tile reaches on MFMA, from the expanded table, and the backward takes
+     the table and bias gradients from an offset-parallel pass (one
+     workgroup per block of 64 offsets sums its diagonals in a fixed order:
+     deterministic, no atomics) instead of a stored offset-gradient buffer.
+     Projection memory and workspace become O(N) per (batch, head) slice
+     (identity maps such as Transformer-XL's otherwise store O(N^2)), at the
+     cost of the per-tile products.  Requires bf16 inputs and the A^Q term;
+     u, v and a scalar bias may be present; A^K, segment masks and dropout
+     are not supported with it (RELPOS_E_UNSUPPORTED).  relpos_project then
+     stores only the per-token entries and the expanded bias, and the
+     relpos_sizes figures shrink accordingly. */
+  int32_t in_tile;
+  int32_t reserved0;       /* must be 0                                      */
 } relpos_desc;
 
 typedef struct relpos_shape {

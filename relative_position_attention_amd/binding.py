@@ -12,7 +12,7 @@ EXPORTED_SYMBOLS = (
     "relpos_set_stage_events", "relpos_project_noalloc",
 )
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAP_KIND = {"identity": 0, "clipped": 1, "t5": 2, "log": 3, "explicit": 4}
 DTYPE = {"f32": 0, "bf16": 1}
 TERM = {"aq": 1, "ak": 2, "bias": 4, "u": 8, "v": 16}
@@ -43,7 +43,8 @@ class _Desc(ctypes.Structure):
                 ("ak_row_stride", ctypes.c_int64), ("ak_head_stride", ctypes.c_int64),
                 ("bias_row_stride", ctypes.c_int64), ("bias_head_stride", ctypes.c_int64),
                 ("segmented", ctypes.c_int32), ("dropout_p8", ctypes.c_int32),
-                ("dropout_seed", ctypes.c_uint64)]
+                ("dropout_seed", ctypes.c_uint64), ("in_tile", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
 
 
 class _Shape(ctypes.Structure):
@@ -133,7 +134,9 @@ class Problem:
     dtype, causal, scale, map, signs, terms, rows, aq_shared, and optionally
     segments (per batch row a list of token intervals [start, end); the
     tensors then carry "seg", see segment_bounds) and dropout
-    ({"p8": drop probability in 1/256, "seed": 64-bit Philox key}).  ``out_dtype``
+    ({"p8": drop probability in 1/256, "seed": 64-bit Philox key}) and
+    in_tile (True: relation products computed inside the tiles, nothing
+    quadratic stored; bf16 inputs with the A^Q term).  ``out_dtype``
     is the dtype of O, dQ, dK, dV ("f32" or "bf16").  ``split_operands``
     sets the descriptor field of that name (bf16 inputs only): P and the
     score gradient enter their MFMA products as bf16 hi + lo pairs, which a
@@ -157,6 +160,7 @@ class Problem:
         d.sign_b = int(signs.get("bias", 1))
         d.split_operands = int(bool(split_operands))
         d.segmented = int(spec.get("segments") is not None)
+        d.in_tile = int(bool(spec.get("in_tile", False)))
         dr = spec.get("dropout")
         if dr is not None:
             d.dropout_p8 = int(dr["p8"])

@@ -93,6 +93,7 @@ std::string plan_key(const relpos_desc* d, const relpos_shape* sh) {
   put(key, d->bias_head_stride);
   put(key, d->segmented);
   put(key, d->dropout_p8);  // (the seed is read per call, not planned)
+  put(key, d->in_tile);
   if (m.kind == RELPOS_MAP_EXPLICIT && m.explicit_rows != nullptr && m.clip >= 0)
     key.append(reinterpret_cast<const char*>(m.explicit_rows),
                sizeof(int32_t) * (2 * static_cast<size_t>(m.clip) + 1));
@@ -260,6 +261,7 @@ int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
       a.S = p.S;
       a.R = R;
       a.causal = p.causal;
+      a.N = p.N;
       RP_HIP(launch_meta_affine(a, s));
     } else {
       // bucketed / explicit maps: the host-built rows travel as kernel
@@ -281,8 +283,14 @@ int build_maps(const Plan& p, void* ws, hipStream_t s, bool with_fold) {
   return RELPOS_OK;
 }
 
-int expand_tables(const Plan& p, const relpos_desc* desc, const relpos_tensors* in, void* ws,
-                  hipStream_t s) {
+// The expanded table A~^Q: in the workspace, or (in-tile products) in z,
+// next to its transpose.
+char* atq_ptr(const Plan& p, void* z, void* ws) {
+  return p.in_tile ? at_off<char>(z, p.z_atq) : at_off<char>(ws, p.ws_atq);
+}
+
+int expand_tables(const Plan& p, const relpos_desc* desc, const relpos_tensors* in, void* z,
+                  void* ws, hipStream_t s) {
   const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
   if (p.aq) {
     ExpandArgs e;
@@ -290,10 +298,12 @@ int expand_tables(const Plan& p, const relpos_desc* desc, const relpos_tensors* 
     e.row_stride = desc->aq_row_stride;
     e.head_stride = desc->aq_head_stride;
     e.beta = at_off<int32_t>(ws, p.ws_beta_q);
-    e.out = at_off<char>(ws, p.ws_atq);
+    e.out = atq_ptr(p, z, ws);
     e.Ht = p.Htq;
     e.S = p.S;
     RP_HIP(launch_expand(dt, e, s));
+    if (p.in_tile)
+      RP_HIP(launch_transpose_rows(e.out, at_off<char>(z, p.z_atqt), p.Htq, p.S, p.Sp, s));
   }
   if (p.ak) {
     ExpandArgs e;
@@ -327,16 +337,16 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
   be.head_stride = desc->bias_head_stride;
   be.beta_b = at_off<int32_t>(ws, p.ws_beta_b);
   be.vb = p.v ? in->vbias : nullptr;
-  be.atq = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+  be.atq = p.aq ? atq_ptr(p, z, ws) : nullptr;
   be.htq_shared = p.aq_shared;
   be.bt = zv.bt;
   be.H = p.H;
   be.S = p.S;
   RP_HIP(launch_bias_expand(dt, be, s));
-  if (p.aq) {
+  if (p.aq && !p.in_tile) {
     ProjectArgs pa;
     pa.x = in->q;
-    pa.at = at_off<char>(ws, p.ws_atq);
+    pa.at = atq_ptr(p, z, ws);
     pa.at_shared = p.aq_shared;
     pa.bt = zv.bt;
     pa.gi = at_off<GroupInfo>(z, p.z_gq);
@@ -374,7 +384,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
   RowKeyArgs rk;
   rk.q = in->q;
   rk.k = in->k;
-  rk.atq = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+  rk.atq = p.aq ? atq_ptr(p, z, ws) : nullptr;
   rk.atk = p.ak ? at_off<char>(ws, p.ws_atk) : nullptr;
   rk.atq_shared = p.aq_shared;
   rk.atk_shared = p.ak_shared;
@@ -411,6 +421,12 @@ AttnArgs attn_args(const Plan& p, const relpos_tensors* in, void* z, void* ws) {
   a.keyhi = zv.keyhi;
   a.keymid = zv.keymid;
   a.bt = zv.bt;
+  if (p.in_tile) {
+    a.at = at_off<char>(z, p.z_atq);
+    a.att = at_off<char>(z, p.z_atqt);
+    a.at_shared = p.aq_shared;
+    a.Sp = p.Sp;
+  }
   a.N = p.N;
   a.H = p.H;
   a.D = p.delta;
@@ -428,7 +444,7 @@ int base_flags(const Plan& p) {
   int f = 0;
   if (p.segmented) f |= F_SEG;
   if (p.drop_p8 > 0) f |= F_DROP;
-  if (p.aq) f |= F_ZQ;
+  if (p.aq) f |= p.in_tile ? F_IT : F_ZQ;
   if (p.ak) f |= F_ZK;
   if (p.bias && !p.aq) f |= F_BT;
   if (p.u) f |= F_U;
@@ -449,7 +465,7 @@ int run_project(const relpos_desc* desc, const relpos_shape* shape, const relpos
   if (!aligned16(z) || !aligned16(ws)) return fail(RELPOS_E_MISALIGNED, "z / ws misaligned");
   if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
   if ((rc = build_maps(p, ws, s, false)) != RELPOS_OK) return rc;
-  if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
+  if ((rc = expand_tables(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   return project_into(p, desc, in, z, ws, s);
 }
 
@@ -523,7 +539,7 @@ int run_fwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     z = at_off<char>(ws, p.ws_fwd_end);
     if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
     if ((rc = build_maps(p, ws, s, false)) != RELPOS_OK) return rc;
-    if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
+    if ((rc = expand_tables(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
     if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   }
   AttnArgs a = attn_args(p, in, z, ws);
@@ -557,6 +573,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if ((p.aq && !gr->daq) || (p.ak && !gr->dak) || (p.bias && !gr->dbias) || (p.u && !gr->du) ||
       (p.v && !gr->dvbias))
     return fail(RELPOS_E_INVALID_ARG, "a table gradient pointer is null");
+  if (p.in_tile) return fail(RELPOS_E_UNSUPPORTED, "in-tile backward not built");
   void* z = const_cast<void*>(zc);
   const size_t need = z ? p.ws_bwd_end : p.ws_bwd_end + p.z_bytes;
   if (ws == nullptr || ws_bytes < need) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
@@ -565,9 +582,12 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
 
   const int dt = p.dtype == RELPOS_DTYPE_F32 ? 0 : 1;
   if ((rc = build_maps(p, ws, s, true)) != RELPOS_OK) return rc;
-  if ((rc = expand_tables(p, desc, in, ws, s)) != RELPOS_OK) return rc;
-  if (z == nullptr) {
-    z = at_off<char>(ws, p.ws_bwd_end);
+  const bool have_z = z != nullptr;
+  if (!have_z) z = at_off<char>(ws, p.ws_bwd_end);
+  // (in-tile products: the expanded tables are part of z, written with it)
+  if (!p.in_tile || !have_z)
+    if ((rc = expand_tables(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
+  if (!have_z) {
     if ((rc = build_groups(p, z, s)) != RELPOS_OK) return rc;
     if ((rc = project_into(p, desc, in, z, ws, s)) != RELPOS_OK) return rc;
   }

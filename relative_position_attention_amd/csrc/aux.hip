@@ -71,7 +71,8 @@ __global__ __launch_bounds__(256) void meta_affine_kernel(AffineMapArgs m) {
   if (s >= m.S) return;
   const int dl = s - m.D;
   int row = -1;
-  if (!(m.causal && dl < 0)) {
+  // (offsets beyond N - 1 in magnitude belong to no pair)
+  if (!(m.causal && dl < 0) && dl <= m.N - 1 && dl >= -(m.N - 1)) {
     const int x = m.sign * dl;
     row = m.kind == RELPOS_MAP_IDENTITY ? x + m.offset : iclamp(x, -m.clip, m.clip) + m.clip;
   }
@@ -751,6 +752,34 @@ hipError_t launch_meta_groups(const MetaArgs& m, hipStream_t s) {
 
 hipError_t launch_meta_fill(const MetaChunk& c, hipStream_t s) {
   hipLaunchKernelGGL(meta_fill_kernel, dim3(1), dim3(256), 0, s, c);
+  return hipGetLastError();
+}
+
+// 64 x 64 tile transpose through LDS (bf16 words): block (cb, h) moves table
+// rows c = 64 cb .. +63 of head h into columns c of dst.
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const u16* src, u16* dst, int S, int Sp) {
+  __shared__ u16 t[64][66];
+  const int cb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const u16* sh = src + static_cast<int64_t>(h) * S * 64;
+  u16* dh = dst + static_cast<int64_t>(h) * 64 * Sp;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int idx = tid + 256 * k, r = idx >> 6, e = idx & 63;
+    const int c = 64 * cb + r;
+    t[r][e] = c < S ? sh[static_cast<int64_t>(c) * 64 + e] : u16(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int idx = tid + 256 * k, e = idx >> 6, r = idx & 63;
+    const int c = 64 * cb + r;
+    if (c < Sp) dh[static_cast<int64_t>(e) * Sp + c] = t[r][e];
+  }
+}
+
+hipError_t launch_transpose_rows(const void* src, void* dst, int Ht, int S, int Sp, hipStream_t s) {
+  hipLaunchKernelGGL(transpose_rows_kernel, dim3(nblk(Sp, 64), Ht), dim3(256), 0, s,
+                     static_cast<const u16*>(src), static_cast<u16*>(dst), S, Sp);
   return hipGetLastError();
 }
 

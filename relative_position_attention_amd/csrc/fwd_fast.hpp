@@ -35,8 +35,11 @@
 // segment), F_DROP dropout (P V takes P times the pair's 0/1 keep mask and O
 // the keep scale; the row sums, hence L, keep P itself; segments are then
 // taken when given), as defined in extras.hpp.
+// F_IT computes the band tiles' Z^Q entries in the tile (intile.hpp)
+// instead of reading stored projections.
 #pragma once
 #include "extras.hpp"
+#include "intile.hpp"
 #include "relation.hpp"
 #include "tiles.hpp"
 
@@ -49,16 +52,18 @@ constexpr int kWQ = 16 * QB;       // queries per wave
 constexpr int kBM = 4 * kWQ;       // queries per workgroup
 constexpr int kKP = 72;            // K and V tile pitch (bf16): 144-byte rows
 constexpr float kLazy = 8.f;       // rescale threshold, log2 units
+constexpr int kZwP = 84;           // in-tile scratch pitch (fp32): 80 window rows
 // an MFMA A operand whose 16 rows are all ones (bf16 1.0 = 0x3f80)
 #define kOnes8 (__builtin_bit_cast(bf16x8, uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}))
 
 template <int F>
-__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || (F & F_DROP) ||
+__global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || (F & F_DROP) || (F & F_IT) ||
                                                   ((F & F_SEG) && (F & F_BT))) ? 2 : 3) void attn_fwd_fast(AttnArgs a, int nqb, int total,
                                                           int xcd_map) {
   constexpr bool CAUSAL = (F & F_CAUSAL) != 0;
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
   constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
+  constexpr bool IT = (F & F_IT) != 0;
   // per-key relation entries: with a key table (F_ZK) the band value and the
   // two boundary values differ per key; with only the Transformer-XL u term
   // they are one value u . k_j
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
   // copies, written so that the store needs no branch)
   __shared__ __attribute__((aligned(16))) float skc[2][4][64];
   __shared__ int sseg[2][4];
+  // in-tile products: one [16 queries][kZwP] window scratch per wave
+  __shared__ __attribute__((aligned(16))) float szw[IT ? 4 * 16 * kZwP : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
@@ -176,6 +183,9 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
     rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+  ItTables itb;
+  if (IT) itb = it_tables(a, h);
+  float* const scr = szw + (IT ? wave * 16 * kZwP : 0);
 
   // key tiles of each block: [0, nkq) visible; region bounds from the
   // block's extreme offsets: tiles [0, n_hi) have delta >= D for every pair,
@@ -371,10 +381,22 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
+        if constexpr (IT) {
+          // the block's 80-row window on MFMA, into the wave's scratch
+          floatx4 zw[5];
+          it_rows<5>(itb, qbase[qb] - j0 - 63 + D, qf[qb][0], qf[qb][1], c16, g, zw);
+          it_put<5>(scr, kZwP, c16, g, zw);
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const int j1 = j0 + 16 * kb + 4 * g;
           float zq[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (IT) {
+            // pair (i, j1 + t) at window row c16 + 63 - 16 kb - 4 g - t
+            const float* zr = scr + c16 * kZwP + c16 + 60 - 16 * kb - 4 * g;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) zq[t] = zr[3 - t];
+          }
           if (F & F_ZQ) {
             uint2 w;
             if (HOIST) {
@@ -431,7 +453,8 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) off[qb] = (side[0] ? rhi[qb] : rlo[qb]) * sl2;
         } else {
-          const bool pure = qbase[0] - (j0 + 63) > -D && qbase[QB - 1] + 15 - j0 < D;
+          // (in-tile products: every pair lies in the band)
+          const bool pure = IT || (qbase[0] - (j0 + 63) > -D && qbase[QB - 1] + 15 - j0 < D);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             off[qb] = 0.f;
@@ -455,7 +478,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
           if (!act[qb]) continue;
           if (sat[qb])
             off[qb] = (side[qb] ? rhi[qb] : rlo[qb]) * sl2;
-          else if (qbase[qb] - (j0 + 63) > -D && qbase[qb] + 15 - j0 < D)
+          else if (IT || (qbase[qb] - (j0 + 63) > -D && qbase[qb] + 15 - j0 < D))
             band_terms(qb, std::true_type{});
           else
             band_terms(qb, std::false_type{});
@@ -615,6 +638,23 @@ hipError_t dispatch_fast(int flags, const AttnArgs& a, int B, hipStream_t s) {
     RP_CASE(F_ZQ | F_ZK | F_U)
     RP_CASE(F_ZK | F_BT | F_U)
 #undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// in-tile products (F_IT): A^Q with or without the u term
+template <int SPL>
+hipError_t dispatch_it(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  switch (flags & (F_IT | F_U | F_CAUSAL)) {
+    case F_IT:
+      return launch_fast<F_IT | SPL>(a, B, s);
+    case F_IT | F_CAUSAL:
+      return launch_fast<F_IT | F_CAUSAL | SPL>(a, B, s);
+    case F_IT | F_U:
+      return launch_fast<F_IT | F_U | SPL>(a, B, s);
+    case F_IT | F_U | F_CAUSAL:
+      return launch_fast<F_IT | F_U | F_CAUSAL | SPL>(a, B, s);
     default:
       return hipErrorInvalidValue;
   }

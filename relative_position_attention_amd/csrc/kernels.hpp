@@ -26,6 +26,7 @@ enum : int {
   F_DZ16 = 512,   // backward: query-side offset gradients stored in fp16
   F_SEG = 1024,   // segment masks (extras.hpp)
   F_DROP = 2048,  // attention dropout, with segment masks when given (extras.hpp)
+  F_IT = 4096,    // in-tile products q . A~^Q from the expanded table (intile.hpp)
 };
 
 struct AttnArgs {
@@ -44,6 +45,11 @@ struct AttnArgs {
   const float* keyhi;
   const float* keymid;
   const float* bt;  // [H, S] expanded bias (b and v folded), fp32
+  // F_IT (in-tile products): the expanded table A~^Q [Ht, S, 64] and its
+  // transpose [Ht, 64, Sp] (bf16), Ht = 1 when shared by the heads
+  const void* at;
+  const void* att;
+  int at_shared, Sp;
   void* o;          // forward output / backward input (out dtype)
   float* lse;       // natural-log logsumexp
   const float* dvec;  // backward: D = rowdot(dO, O)
@@ -86,6 +92,8 @@ hipError_t launch_attn_fwd_bf16_seg(int flags, const AttnArgs& a, int B, hipStre
 hipError_t launch_bwd_q_bf16_seg(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16_seg(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_fwd_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
+// in-tile products (F_IT: fwd_it.hip, bwd_q_it.hip, bwd_k_it.hip, off_pass.hip)
+hipError_t launch_attn_fwd_bf16_it(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_q_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
 
@@ -115,9 +123,13 @@ struct AffineMapArgs {
   int32_t* beta;      // [S]
   int kind;           // RELPOS_MAP_IDENTITY or RELPOS_MAP_CLIPPED
   int sign, offset, clip;
-  int D, S, R, causal;
+  int D, S, R, causal, N;
 };
 hipError_t launch_meta_affine(const AffineMapArgs& m, hipStream_t s);
+
+// dst[h][e][c] = src[h][c][e] for c < S (bf16 rows of 64), zero for
+// S <= c < Sp: the transposed expanded table of the in-tile products
+hipError_t launch_transpose_rows(const void* src, void* dst, int Ht, int S, int Sp, hipStream_t s);
 
 // fold[r] = first and last expanded row s with beta(s) = r ([1, 0] if none)
 hipError_t launch_fold_meta(const int32_t* beta, int32_t* fold, int S, int R, hipStream_t s);

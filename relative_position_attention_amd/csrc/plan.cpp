@@ -313,6 +313,27 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     detail = "dropout_p8 must be in 0..255";
     return RELPOS_E_INVALID_ARG;
   }
+  if ((desc->in_tile != 0 && desc->in_tile != 1) || desc->reserved0 != 0) {
+    detail = "in_tile must be 0 or 1 and reserved0 0";
+    return RELPOS_E_INVALID_ARG;
+  }
+  if (desc->in_tile) {
+    // the in-tile kernels compute q . A~^Q per tile (bf16 MFMA) and take the
+    // table gradient from the offset-parallel pass
+    const char* why = nullptr;
+    if (desc->dtype != RELPOS_DTYPE_BF16)
+      why = "in_tile needs bf16 inputs";
+    else if (!(desc->terms & RELPOS_TERM_AQ))
+      why = "in_tile needs the A^Q term (a scalar bias alone has no projections)";
+    else if (desc->terms & RELPOS_TERM_AK)
+      why = "in_tile does not support the A^K term";
+    else if (desc->segmented || desc->dropout_p8 > 0)
+      why = "in_tile does not support segment masks or dropout";
+    if (why != nullptr) {
+      detail = why;
+      return RELPOS_E_UNSUPPORTED;
+    }
+  }
   if (!std::isfinite(desc->scale) || !(desc->scale > 0.f)) {
     detail = "scale must be finite and positive";
     return RELPOS_E_INVALID_ARG;
@@ -347,6 +368,7 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.split = desc->split_operands != 0 && p.dtype == RELPOS_DTYPE_BF16;
   p.segmented = desc->segmented != 0;
   p.drop_p8 = desc->dropout_p8;
+  p.in_tile = desc->in_tile != 0;
   bool any_table = p.aq || p.ak || p.bias;
   if (any_table && p.R < 1) {
     detail = "num_rows must be >= 1";
@@ -403,6 +425,11 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     }
     D = std::max(D, d);
   }
+  // In-tile products: every pair is a band pair (D > N - 1, so no saturated
+  // tiles and no boundary entries), and D = 15 mod 16 with D >= N + 3, so a
+  // 16-query block's row window against a 64-key tile starts on a multiple of
+  // 16 (aligned table loads) and the last four expanded rows are unreachable.
+  if (p.in_tile) D = (p.N + 3) + ((15 - (p.N + 3) % 16) + 16) % 16;
   p.delta = D;
   p.S = 2 * D + 1;
   p.NG = (p.N + kGroup - 1) / kGroup;
@@ -414,6 +441,7 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
     for (int s = 0; s < p.S; ++s) {
       int delta = s - D;
       if (p.causal && delta < 0) continue;  // unreachable under the mask
+      if (delta > p.N - 1 || delta < -(p.N - 1)) continue;  // no pair has this offset
       int64_t r;
       if (!map_row(desc->map, static_cast<int64_t>(sign) * delta, r)) {
         detail = "malformed map parameters";
@@ -456,7 +484,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.Htq = p.aq ? (p.aq_shared ? 1 : p.H) : 0;
   p.Htk = p.ak ? (p.ak_shared ? 1 : p.H) : 0;
   p.need_qside = p.aq || p.bias || p.v;
-  if (p.need_qside && !build_side(p, true, detail)) return RELPOS_E_UNSUPPORTED;
+  // (in-tile: no stored projections, hence no group layouts)
+  if (p.need_qside && !p.in_tile && !build_side(p, true, detail)) return RELPOS_E_UNSUPPORTED;
   if (p.ak && !build_side(p, false, detail)) return RELPOS_E_UNSUPPORTED;
   // per-slice bytes at the entry widths: Z (z_size) on either side, and the
   // one offset-gradient buffer (the larger side's elements at the wider
@@ -488,6 +517,9 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   // the longest blocks are split four ways
   if (p.causal) want = std::max(want, 4);
   p.nchunk = std::max(1, std::min(want, subs));
+  // in-tile: the offset-parallel pass writes one partial per batch row
+  if (p.in_tile) p.nchunk = p.B;
+  p.Sp = (p.S + 7) & ~7;
 
   // ---- z layout (group tables first)
   size_t off = 0;
@@ -496,7 +528,7 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   p.z_gk = off;
   off = align256(off + sizeof(GroupInfo) * p.NG);
   const size_t bhn4 = static_cast<size_t>(p.BH) * p.N * 4;
-  if (p.aq) {
+  if (p.aq && !p.in_tile) {
     p.z_zq = off;
     off = align256(off + static_cast<size_t>(p.BH) * p.zq.bh_elems * p.z_size);
   }
@@ -516,6 +548,15 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   off = align256(off + bhn4);
   p.z_bt = off;
   off = align256(off + static_cast<size_t>(p.H) * p.S * 4);
+  if (p.in_tile) {
+    // the expanded table A~^Q ([Htq, S, 64]) and its transpose ([Htq, 64, Sp],
+    // columns past S zero) travel with the per-token entries: the in-tile
+    // passes read them instead of projections
+    p.z_atq = off;
+    off = align256(off + static_cast<size_t>(p.Htq) * p.S * kHeadDim * p.t_size);
+    p.z_atqt = off;
+    off = align256(off + static_cast<size_t>(p.Htq) * kHeadDim * p.Sp * p.t_size);
+  }
   p.z_bytes = off;
 
   // ---- workspace, forward part
@@ -530,7 +571,7 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
   off = align256(off + 3 * static_cast<size_t>(std::max(p.R, 1)) * 2 * 4);
   p.ws_fold_list = off;  // three [S] index lists (tables with listed folds)
   off = align256(off + 3 * static_cast<size_t>(p.S) * 4);
-  if (p.aq) {
+  if (p.aq && !p.in_tile) {
     p.ws_atq = off;
     off = align256(off + static_cast<size_t>(p.Htq) * p.S * kHeadDim * p.t_size);
   }

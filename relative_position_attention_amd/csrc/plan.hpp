@@ -49,6 +49,8 @@ struct Plan {
   bool split = false;  // P and G as bf16 hi + lo pairs in their MFMA products
   bool segmented = false;  // segment mask (tensors->seg)
   int drop_p8 = 0;         // dropout probability in units of 1/256
+  bool in_tile = false;    // relation products computed per tile (no stored Z)
+  int Sp = 0;              // row pitch of the transposed expanded table (S rounded up to 8)
   int nchunk = 1;  // token chunks per head in the table-gradient reduction
   // Per table (A^Q, A^K, b): rows that are not one interval of expanded rows
   // fold through an index list (fold_rows: [R, 2] first / last position of
@@ -58,7 +60,7 @@ struct Plan {
 
   // ---- byte offsets inside z ----
   size_t z_gq = 0, z_gk = 0, z_zq = 0, z_zk = 0, z_rowlo = 0, z_rowhi = 0, z_keylo = 0, z_keyhi = 0,
-         z_keymid = 0, z_bt = 0, z_bytes = 0;
+         z_keymid = 0, z_bt = 0, z_atq = 0, z_atqt = 0, z_bytes = 0;
   // ---- byte offsets inside ws (forward part) ----
   size_t ws_beta_q = 0, ws_beta_k = 0, ws_beta_b = 0, ws_fold = 0, ws_fold_list = 0,
          ws_atq = 0, ws_atk = 0, ws_fwd_end = 0;
