@@ -573,7 +573,6 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if ((p.aq && !gr->daq) || (p.ak && !gr->dak) || (p.bias && !gr->dbias) || (p.u && !gr->du) ||
       (p.v && !gr->dvbias))
     return fail(RELPOS_E_INVALID_ARG, "a table gradient pointer is null");
-  if (p.in_tile) return fail(RELPOS_E_UNSUPPORTED, "in-tile backward not built");
   void* z = const_cast<void*>(zc);
   const size_t need = z ? p.ws_bwd_end : p.ws_bwd_end + p.z_bytes;
   if (ws == nullptr || ws_bytes < need) return fail(RELPOS_E_WORKSPACE_TOO_SMALL, "workspace too small");
@@ -642,8 +641,11 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   if (p.segmented && (p.need_qside || p.ak)) RP_HIP(launch_zero(dz, dz_bytes, s));
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
-  const int qflags = bf | (p.need_qside ? F_DZQ : 0) | (p.dzq_f32 ? F_DZ32 : 0) |
-                     (p.dzq_f16 ? F_DZ16 : 0);
+  // (in-tile products: the query pass adds the relation part of dQ itself and
+  // writes no offset gradients; the offset-parallel pass below makes the
+  // table sums)
+  const bool qside_dz = p.need_qside && !p.in_tile;
+  const int qflags = bf | (qside_dz ? F_DZQ | (p.dzq_f32 ? F_DZ32 : 0) | (p.dzq_f16 ? F_DZ16 : 0) : 0);
   if (dt == 0)
     RP_HIP(launch_attn_bwd_q_f32(qflags, a, p.B, s));
   else
@@ -653,11 +655,12 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     FinalizeArgs f;
     std::memset(&f, 0, sizeof f);
     f.acc = dqacc;
-    f.dz = p.aq ? dz : nullptr;
+    const bool qtab = p.aq && !p.in_tile;
+    f.dz = qtab ? dz : nullptr;
     f.dz_bh = a.dz_bh;
-    f.gi = p.need_qside ? at_off<GroupInfo>(z, p.z_gq) : nullptr;
-    f.bnd = p.aq ? bndq : nullptr;
-    f.at = p.aq ? at_off<char>(ws, p.ws_atq) : nullptr;
+    f.gi = qside_dz ? at_off<GroupInfo>(z, p.z_gq) : nullptr;
+    f.bnd = qtab ? bndq : nullptr;
+    f.at = qtab ? at_off<char>(ws, p.ws_atq) : nullptr;
     f.at_shared = p.aq_shared;
     f.out = gr->dq;
     f.N = p.N;
@@ -675,28 +678,32 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
       RP_HIP(launch_finalize_bf16(f, p.BH, s));
   }
   if (p.need_qside) {
-    PartialArgs pa;
-    pa.dz = dz;
-    pa.dz_bh = a.dz_bh;
-    pa.gi = at_off<GroupInfo>(z, p.z_gq);
-    pa.bnd = bndq;
-    pa.x = in->q;
-    pa.p1 = p.aq ? p1 : nullptr;
-    pa.p2 = (p.bias || p.v) ? p2 : nullptr;
-    pa.B = p.B;
-    pa.N = p.N;
-    pa.H = p.H;
-    pa.D = p.delta;
-    pa.S = p.S;
-    pa.nchunk = p.nchunk;
-    pa.key_side = 0;
-    pa.causal = p.causal;
-    pa.dz_f32 = p.dzq_f32;
-    pa.dz_f16 = p.dzq_f16;
-    if (dt == 0)
-      RP_HIP(launch_partials_f32(pa, s));
-    else
-      RP_HIP(launch_partials_bf16(pa, s));
+    if (p.in_tile) {
+      RP_HIP(launch_offset_pass_it(a, p.B, p.causal, p.u, p1, p2, s));
+    } else {
+      PartialArgs pa;
+      pa.dz = dz;
+      pa.dz_bh = a.dz_bh;
+      pa.gi = at_off<GroupInfo>(z, p.z_gq);
+      pa.bnd = bndq;
+      pa.x = in->q;
+      pa.p1 = p.aq ? p1 : nullptr;
+      pa.p2 = (p.bias || p.v) ? p2 : nullptr;
+      pa.B = p.B;
+      pa.N = p.N;
+      pa.H = p.H;
+      pa.D = p.delta;
+      pa.S = p.S;
+      pa.nchunk = p.nchunk;
+      pa.key_side = 0;
+      pa.causal = p.causal;
+      pa.dz_f32 = p.dzq_f32;
+      pa.dz_f16 = p.dzq_f16;
+      if (dt == 0)
+        RP_HIP(launch_partials_f32(pa, s));
+      else
+        RP_HIP(launch_partials_bf16(pa, s));
+    }
     if (p.aq) {
       FoldArgs fa;
       fa.p1 = p1;
@@ -732,7 +739,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
     if (p.v) {
       DvArgs dv;
       dv.db = db;
-      dv.atq = at_off<char>(ws, p.ws_atq);
+      dv.atq = atq_ptr(p, z, ws);
       dv.at_shared = p.aq_shared;
       dv.part = red;
       dv.out = gr->dvbias;

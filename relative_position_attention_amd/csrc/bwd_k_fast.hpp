@@ -28,8 +28,11 @@
 // workgroup's keys' segments, per-pair tests elsewhere), F_DROP dropout
 // (G' = P (dP keep - D), dV takes P keep; segments are then taken when
 // given), as defined in extras.hpp.
+// F_IT computes the tiles' Z^Q entries in the tile (intile.hpp) instead of
+// staging stored projections.
 #pragma once
 #include "extras.hpp"
+#include "intile.hpp"
 #include "relation.hpp"
 #include "tiles.hpp"
 
@@ -39,6 +42,7 @@ namespace {
 
 constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
 constexpr int kT = 32;  // queries per tile
+constexpr int kKwP = 36;  // in-tile scratch pitch (fp32): 32 window rows
 
 template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int total, int xcd_map) {
@@ -50,6 +54,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   constexpr bool DZ = (F & F_DZK) != 0;
   constexpr bool CS = (F & F_U) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
+  constexpr bool IT = (F & F_IT) != 0;
   // query projections of a band tile are staged into LDS once per workgroup
   constexpr bool STZQ = (F & F_ZQ) != 0;
   // causal masks: pair each 16-key block with its mirror (below)
@@ -62,6 +67,8 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   // so that the store needs no branch)
   __shared__ __attribute__((aligned(16))) float sqs[2][8][kT];
   __shared__ int sseg[2][4];
+  // in-tile products: one [16 queries][kKwP] window scratch per wave
+  __shared__ __attribute__((aligned(16))) float szw[IT ? 4 * 16 * kKwP : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
@@ -150,6 +157,9 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+  ItTables itb;
+  if (IT) itb = it_tables(a, h);
+  float* const scr = szw + (IT ? wave * 16 * kKwP : 0);
 
   // query tiles: causal starts at the workgroup's first key; a block's tiles
   // before its own first key are fully masked and skipped.  Regions from the
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int ja = jbase[PAIR ? kb : 0], jz = jbase[PAIR ? kb : 1] + 15;
-        pure[kb] = i0 - jz > -D && i0 + kT - 1 - ja < D;
+        pure[kb] = IT || (i0 - jz > -D && i0 + kT - 1 - ja < D);
       }
       bool need_mask[2];
 #pragma unroll
@@ -427,11 +437,29 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
             if (STZQ)  // Z^Q[i1 + t][i1 + t - j + D], t = 0..3
               zq4 = __builtin_bit_cast(halfx4, lds_tr4(reinterpret_cast<const bf16*>(szq[buf]), kZP,
                                                        16 * qb + 4 * g, jloc[kb], c16));
+            float zi[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (IT) {
+              // the 32-row window of query block qb against key block kb
+              // (rows sb + 0..31, sb = i0 + 16 qb - jbase[kb] - 15 + D) on
+              // MFMA, through the wave's scratch; pair (i1 + t, j) sits at
+              // window row 4 g + t - c16 + 15 of query row 4 g + t
+              bf16x8 q2[2];
+#pragma unroll
+              for (int c = 0; c < 2; ++c)
+                q2[c] = *reinterpret_cast<const bf16x8*>(Qs + (16 * qb + c16) * kP + 32 * c + 8 * g);
+              floatx4 zw[2];
+              it_rows<2>(itb, i0 + 16 * qb - jbase[kb] - 15 + D, q2[0], q2[1], c16, g, zw);
+              it_put<2>(scr, kKwP, c16, g, zw);
+              const float* zr = scr + (4 * g) * (kKwP + 1) + 15 - c16;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) zi[t] = zr[t * (kKwP + 1)];
+            }
             if (pure[kb]) {
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
                 float band = kmid[kb] + zk[t];
                 if (F & F_ZQ) band += static_cast<float>(zq4[t]);
+                if (IT) band += zi[t];
                 if (F & F_BT)
                   band += bloadf(rbt, static_cast<uint32_t>(iclamp(i1 + t - j + D, 0, 2 * D) * 4));
                 rel[t] = band;
@@ -673,6 +701,23 @@ hipError_t dispatch_kf(int flags, const AttnArgs& a, int B, hipStream_t s) {
     return launch_kf<(X) | F_CAUSAL | SPL>(a, B, s);
     RP_KF_FLAGS(RP_CASE)
 #undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// in-tile products (F_IT): A^Q with or without the u term
+template <int SPL>
+hipError_t dispatch_kit(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  switch (flags & (F_IT | F_U | F_CAUSAL)) {
+    case F_IT:
+      return launch_kf<F_IT | SPL>(a, B, s);
+    case F_IT | F_CAUSAL:
+      return launch_kf<F_IT | F_CAUSAL | SPL>(a, B, s);
+    case F_IT | F_U:
+      return launch_kf<F_IT | F_U | SPL>(a, B, s);
+    case F_IT | F_U | F_CAUSAL:
+      return launch_kf<F_IT | F_U | F_CAUSAL | SPL>(a, B, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -6,6 +6,7 @@
 namespace relpos {
 
 hipError_t launch_bwd_q_bf16(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  if (flags & F_IT) return launch_bwd_q_bf16_it(flags, a, B, s);
   if (flags & F_DROP) return launch_bwd_q_bf16_drop(flags, a, B, s);
   if (flags & F_SEG) return launch_bwd_q_bf16_seg(flags, a, B, s);
   if (flags & F_SPLIT) return dispatch_qf<F_SPLIT>(flags, a, B, s);

@@ -21,8 +21,12 @@
 // workgroup's segments, per-pair tests elsewhere), F_DROP dropout (dP takes
 // the pair's keep factor: G' = P (dP keep - D); segments are then taken when
 // given), as defined in extras.hpp.
+// F_IT computes the band tiles' Z^Q entries in the tile and adds the
+// relation part of dQ, sum over the window rows of G A~[s], on MFMA in the
+// tile (intile.hpp), instead of reading projections and writing dZ~^Q.
 #pragma once
 #include "extras.hpp"
+#include "intile.hpp"
 #include "relation.hpp"
 #include "tiles.hpp"
 
@@ -31,6 +35,9 @@ namespace relpos {
 namespace {
 
 constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
+// in-tile scratch pitch (fp32): 80 window rows, or a G' row with its zero
+// margins (32 + 64 + 16 entries)
+constexpr int kQwP = 116;
 
 template <int F>
 __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int total, int xcd_map) {
@@ -41,6 +48,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   constexpr bool DZ = (F & F_DZQ) != 0;
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
+  constexpr bool IT = (F & F_IT) != 0;
   using GT = std::conditional_t<(F & F_DZ16) != 0, _Float16,
                                 typename DzType<bf16, (F & F_DZ32) != 0>::type>;
   // key projections of a band tile are staged into LDS once per workgroup
@@ -53,6 +61,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   __shared__ __attribute__((aligned(16))) bf16 sv[2][64 * kP];
   __shared__ __attribute__((aligned(16))) float skc[2][3][64];
   __shared__ int sseg[2][4];
+  // in-tile products: one [16 queries][kQwP] scratch per wave
+  __shared__ __attribute__((aligned(16))) float szw[IT ? 4 * 16 * kQwP : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
@@ -154,6 +164,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
     rzk = make_rsrc(reinterpret_cast<const _Float16*>(a.zk) + bh * a.zk_bh,
                     static_cast<uint64_t>(a.zk_bh) * 2);
   if (F & F_BT) rbt = make_rsrc(a.bt + static_cast<int64_t>(h) * a.S, static_cast<uint64_t>(a.S) * 4);
+  ItTables itb;
+  if (IT) itb = it_tables(a, h);
+  float* const scr = szw + (IT ? wave * 16 * kQwP : 0);
   // offset gradients through a buffer resource: 32-bit element offsets (no
   // 64-bit row pointers to keep in registers) and range-checked stores
   const Rsrc rdz = make_rsrc(DZ ? reinterpret_cast<GT*>(a.dz) + static_cast<int64_t>(bh) * a.dz_bh : nullptr,
@@ -326,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qa = qbase[PAIR ? qb : 0], qz = qbase[PAIR ? qb : 1] + 15;
-        pure[qb] = qa - (j0 + 63) > -D && qz - j0 < D;
+        pure[qb] = IT || (qa - (j0 + 63) > -D && qz - j0 < D);
       }
       float off[2];
       // transposing-read address of this lane in szk (lds_tr4 with row0 = 4g)
@@ -338,6 +351,12 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         // without a key table (room in the registers): the block's four Z^Q
         // runs are requested together, one memory round trip per block
         // instead of four (every tile of an identity map is a band tile)
+        if constexpr (IT) {
+          // the block's 80-row window on MFMA, into the wave's scratch
+          floatx4 zt[5];
+          it_rows<5>(itb, qbase[qb] - j0 - 63 + D, qf[qb][0], qf[qb][1], c16, g, zt);
+          it_put<5>(scr, kQwP, c16, g, zt);
+        }
         uint2 zw[4];
         if constexpr (HOISTQ) {
 #pragma unroll
@@ -351,6 +370,12 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         for (int kb = 0; kb < 4; ++kb) {
           const int j1 = j0 + 16 * kb + 4 * g;
           float zq[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (IT) {
+            // pair (i, j1 + t) at window row c16 + 63 - 16 kb - 4 g - t
+            const float* zr = scr + c16 * kQwP + c16 + 60 - 16 * kb - 4 * g;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) zq[t] = zr[3 - t];
+          }
           if (F & F_ZQ) {
             uint2 w;
             if constexpr (HOISTQ) {
@@ -499,6 +524,41 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         }
       }
 
+      // in-tile: dQ^T += A~_window^T G'_window^T.  Block qb's G' goes into
+      // the scratch as rows [query][32 + key] between zero margins, so that
+      // window row s'' = 32 k + 8 g + e (e = 0..7) of query c16, which holds
+      // the pair with key j0 + 63 + c16 - s'', is column 95 + c16 - s''; the
+      // table side is A~^T[16 db + c16][sb + 32 k + 8 g ..] (sb = the
+      // window's first row, a multiple of 16: aligned 16-byte loads)
+      if constexpr (IT) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!act[qb]) continue;
+          float* row = scr + c16 * kQwP;
+          const floatx4 z4 = floatx4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<floatx4*>(row + 8 * g) = z4;
+          *reinterpret_cast<floatx4*>(row + 8 * g + 4) = z4;
+          *reinterpret_cast<floatx4*>(row + 96 + 4 * g) = z4;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<floatx4*>(row + 32 + 16 * kb + 4 * g) = s[qb][kb];
+          const int sb = qbase[qb] - j0 - 63 + D;
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            const float* gr = row + 88 + c16 - 32 * k - 8 * g;  // e = 7 .. 0
+            bf16x8 gw;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gw[e] = static_cast<bf16>(gr[7 - e]);
+            const int col = sb + 32 * k + 8 * g;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              const bf16x8 at8 = __builtin_bit_cast(
+                  bf16x8, bload16(itb.att, col >= 0 ? static_cast<uint32_t>((16 * db + c16) * a.Sp + col) * 2 : kOob));
+              dq[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at8, gw, dq[qb][db], 0, 0, 0);
+            }
+          }
+        }
+      }
+
       // dQ^T += K^T G'^T
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -589,6 +649,23 @@ hipError_t dispatch_qf(int flags, const AttnArgs& a, int B, hipStream_t s) {
     return launch_qf<(X) | F_CAUSAL | SPL>(a, B, s);
     RP_QF_FLAGS(RP_CASE)
 #undef RP_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// in-tile products (F_IT): A^Q with or without the u term
+template <int SPL>
+hipError_t dispatch_qit(int flags, const AttnArgs& a, int B, hipStream_t s) {
+  switch (flags & (F_IT | F_U | F_CAUSAL)) {
+    case F_IT:
+      return launch_qf<F_IT | SPL>(a, B, s);
+    case F_IT | F_CAUSAL:
+      return launch_qf<F_IT | F_CAUSAL | SPL>(a, B, s);
+    case F_IT | F_U:
+      return launch_qf<F_IT | F_U | SPL>(a, B, s);
+    case F_IT | F_U | F_CAUSAL:
+      return launch_qf<F_IT | F_U | F_CAUSAL | SPL>(a, B, s);
     default:
       return hipErrorInvalidValue;
   }
