@@ -340,7 +340,50 @@ def extras(torch, rpa, synth, flush, steps=5, warmup=2):
                             warmup, flush))
     out.append(time_variant("recomputed projections", spec0, arr0, torch, rpa, False, steps,
                             warmup, flush, retain=False))
-    return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out}
+    # In-tile relation products ([RPA] §6, Table 7 row "Projections"): the
+    # Transformer-XL shapes (identity map: stored projections are quadratic)
+    # with stored and with in-tile products
+    it_rows = []
+    for label, spec_arr in (("txl B1 H8 N8192 causal", synth.make_bench("txl")),
+                            ("txl B1 H8 N16384 non-causal", synth.make_config(5))):
+        spec, arr = spec_arr
+        it_rows.append(time_variant(label + ", stored", spec, arr, torch, rpa, False, steps, warmup,
+                                    flush))
+        it_rows.append(time_variant(label + ", in-tile", dict(spec, in_tile=True), arr, torch, rpa,
+                                    False, steps, warmup, flush))
+    return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out, "in_tile_rows": it_rows}
+
+
+def cpu_baseline(mechs):
+    """The fp64 oracle on one (batch, head) slice of each mechanism's bench
+    shape, timed on the host; credited FLOPs of those slices per second."""
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    total_s, total_flops, rounds = 0.0, 0.0, 0
+    problems = {}
+    # whole rounds over the mechanisms until at least 10 s of oracle work
+    while rounds < 4 and (rounds == 0 or total_s < 10.0):
+        for name in mechs:
+            if name not in problems:
+                kw = dict(synth.BENCH_SHAPES[name])
+                problems[name] = synth.make_problem(**dict(kw, B=1, H=1))
+            spec, arr = problems[name]
+            t0 = time.perf_counter()
+            oracle.slice_forward_backward(spec, arr, 0, 0)
+            total_s += time.perf_counter() - t0
+            f, b = credited_flops(spec)
+            total_flops += f + b
+        rounds += 1
+    return {"value": total_flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{rounds} x one (batch, head) slice of each of {','.join(mechs)} at N=8192, "
+                      f"fp64 forward+backward ({total_s:.1f} s)"}
 
 
 def cpu_model():

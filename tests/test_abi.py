@@ -193,3 +193,52 @@ def test_t5_descriptors_take_split_operands():
     for idx in (1, 3, 4, 5):
         spec = make_problem(**dict(CONFIGS[idx], N=64))[0]
         assert not split_operands_for(spec), idx
+
+
+@needs_lib
+def test_in_tile_plan_is_linear_in_n():
+    # [RPA] §6 / Table 7 "Projections": with in-tile products nothing
+    # quadratic is stored.  Transformer-XL (identity map over 2N - 1 offsets):
+    # the stored plan's projections and offset-gradient buffer grow as N^2,
+    # the in-tile plan's buffers as N.
+    sizes = {}
+    for N in (2048, 4096, 8192):
+        spec = _spec_small(5, N)
+        st = rpa.Problem(spec).sizes()
+        it = rpa.Problem(dict(spec, in_tile=True)).sizes()
+        sizes[N] = (st, it)
+        D = it["delta"]
+        assert D >= N + 3 and D % 16 == 15          # every pair in the band, aligned windows
+        assert it["expanded_rows"] == 2 * D + 1
+    assert sizes[8192][0]["z_bytes"] / sizes[2048][0]["z_bytes"] > 14.0   # ~16x: quadratic
+    for key in ("z_bytes", "bwd_ws_bytes", "bwd_ws_bytes_noz"):
+        r_it = sizes[8192][1][key] / sizes[2048][1][key]
+        assert r_it < 4.5, (key, r_it)               # ~4x: linear
+        assert sizes[8192][1][key] < sizes[8192][0][key] / 10, key
+
+
+@needs_lib
+def test_in_tile_plan_past_the_slice_limit():
+    # non-causal Transformer-XL at N = 32768: a stored projection slice needs
+    # more than 2^31 bytes (rejected); the in-tile plan has no such slice
+    spec = _spec_small(5, 32768)
+    with pytest.raises(rpa.RelposError) as ei:
+        rpa.Problem(spec).sizes()
+    assert ei.value.code == -2
+    sz = rpa.Problem(dict(spec, in_tile=True)).sizes()
+    assert sz["z_bytes"] < 64 * 2**20
+
+
+@needs_lib
+def test_in_tile_validation():
+    txl = _spec_small(4, 300)
+    assert _err(dict(txl, in_tile=True), in_tile=2) == -1          # not 0/1
+    assert _err(dict(txl, in_tile=True), reserved0=1) == -1
+    f32 = _spec_small(1, 128)                                       # fp32 Shaw
+    assert _err(dict(f32, in_tile=True)) == -2
+    t5 = _spec_small(2, 256)                                        # bias only: no projections
+    assert _err(dict(t5, in_tile=True)) == -2
+    deb = _spec_small(3, 300)                                       # A^K
+    assert _err(dict(deb, in_tile=True)) == -2
+    assert _err(dict(txl, in_tile=True, segments=[[(0, 300)]])) == -2
+    assert _err(dict(txl, in_tile=True, dropout={"p8": 10, "seed": 1})) == -2

@@ -53,3 +53,26 @@ def test_causal_credit_counts_visible_pairs():
     assert fwd == pytest.approx(4 * 64 * visible)
     assert bwd == pytest.approx(2 * fwd)
     assert bench.pair_flops(spec) == pytest.approx(2 * 64 * visible)
+
+
+def test_bench_calls_only_defined_names():
+    # every bare name bench.py calls is defined somewhere in it (a function,
+    # an import or an assignment) or is a builtin: a deleted helper fails here
+    # instead of in the timed run
+    import ast
+    import builtins
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    tree = ast.parse(src)
+    defined = set(dir(builtins))
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            defined.add(node.name)
+            defined.update(a.arg for a in node.args.args + node.args.kwonlyargs) if isinstance(node, ast.FunctionDef) else None
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            defined.update((a.asname or a.name).split(".")[0] for a in node.names)
+        elif isinstance(node, ast.Name) and isinstance(node.ctx, ast.Store):
+            defined.add(node.id)
+        elif isinstance(node, ast.arg):
+            defined.add(node.arg)
+    called = {n.func.id for n in ast.walk(tree) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
+    assert called <= defined, sorted(called - defined)

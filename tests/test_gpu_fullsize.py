@@ -100,3 +100,17 @@ def test_bench_shaw_table_gradient():
     spec, arr = make_problem(**kw)
     got = run_library(spec, arr)
     _compare(_problem(spec, arr), got, [(0, 0)], [0], "bench-shaw-1slice")
+
+
+@pytest.mark.parametrize("idx,slices,table_heads", [
+    (4, [(0, 0), (0, 7)], [0, 7]),                         # TXL causal B1 H8 N8192
+    (5, [(0, 3)], [3]),                                    # TXL B1 H8 N16384
+])
+def test_config_full_size_in_tile(idx, slices, table_heads):
+    # the same configurations with in-tile relation products ([RPA] §6,
+    # Table 7 row "Projections"): no stored projections or offset gradients
+    spec, arr = make_config(idx)
+    spec = dict(spec, in_tile=True)
+    print(f"[full] cfg{idx} in-tile B={spec['B']} H={spec['H']} N={spec['N']}", flush=True)
+    got = run_library(spec, arr)
+    _compare(_problem(spec, arr), got, slices, table_heads, f"cfg{idx}-in-tile")
