@@ -59,7 +59,8 @@ template <bool CAUSAL, bool U>
 __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, float* p2, int nob,
                                                       int BH, int nchunk) {
   // per wave: [0, 16 kOP) scratch, then the query tile (bf16) and the keys'
-  // u . k entries; after the loop the same memory holds the wave's partial
+  // u . k entries (128); after the loop the same memory holds the wave's
+  // partial
   __shared__ __attribute__((aligned(16))) float sred[4][64 * 64];
   __shared__ float sdb[4][64];
 
@@ -82,6 +83,11 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
   const Rsrc rdo = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + tok * 64, slice_bytes);
   const Rsrc rk = make_rsrc(reinterpret_cast<const bf16*>(a.k) + tok * 64, slice_bytes);
   const Rsrc rv = make_rsrc(reinterpret_cast<const bf16*>(a.v) + tok * 64, slice_bytes);
+  // per-token values of the slice (reads past N return zero)
+  const uint64_t row_bytes = static_cast<uint64_t>(N) * 4;
+  const Rsrc rlse = make_rsrc(a.lse + tok, row_bytes);
+  const Rsrc rdd = make_rsrc(a.dvec + tok, row_bytes);
+  const Rsrc rkm = make_rsrc(a.keymid + tok, row_bytes);
   const ItTables itb = it_tables(a, h);
 
   float* const scr = &sred[wave][0];
@@ -103,6 +109,17 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
       if (qw > i_hi || qw + 15 < i_lo) continue;  // (uniform per wave; no barrier in the loop)
       const int i = qw + c16;
       const int jb = qw - dl0 - 63;
+      // Every load of the step is issued here, unconditionally (range-checked
+      // buffer loads), the per-token values first: loads complete in order,
+      // so the waits for the early ones leave the row loads in flight.
+      const float lse_i = bloadf(rlse, static_cast<uint32_t>(i) * 4);
+      const float dd_i = bloadf(rdd, static_cast<uint32_t>(i) * 4);
+      float km1 = 0.f, km2 = 0.f;
+      if (U) {
+        const int j1 = jb + lane, j2 = jb + 64 + lane;
+        km1 = bloadf(rkm, j1 >= 0 ? static_cast<uint32_t>(j1) * 4 : kOob);
+        km2 = bloadf(rkm, j2 >= 0 ? static_cast<uint32_t>(j2) * 4 : kOob);
+      }
       bf16x8 qf[2], df[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -111,8 +128,8 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
         df[c] = __builtin_bit_cast(bf16x8, bload16(rdo, off));
       }
       const bool iok = i < N;
-      const float l2 = iok ? a.lse[tok + i] * kLog2e : INFINITY;
-      const float dd = iok ? a.dvec[tok + i] : 0.f;
+      const float l2 = iok ? lse_i * kLog2e : INFINITY;
+      const float dd = dd_i;
 
       // S and dP over the 80-key rectangle (keys jb + 16 kb + 4 g + t)
       floatx4 sr[5], pr[5];
@@ -144,9 +161,9 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
         *reinterpret_cast<uint4*>(sq + c16 * kOQP + 32 * c + 8 * g) =
             bf16x8_to_f16x8(__builtin_bit_cast(uint4, qf[c]));
       if (U) {
-        const int j1 = jb + lane, j2 = jb + 64 + lane;
-        skm[lane] = (j1 >= 0 && j1 < N) ? a.keymid[tok + j1] : 0.f;
-        if (lane < 16) skm[64 + lane] = (j2 >= 0 && j2 < N) ? a.keymid[tok + j2] : 0.f;
+        // keys jb .. jb + 127 (the rectangle uses the first 80)
+        skm[lane] = km1;
+        skm[64 + lane] = km2;
       }
 
       // rectangle -> (query, offset): offset 16 w + 4 g + t of query c16 is
@@ -181,6 +198,8 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
           const float band = km + zd[w][t];
           const float sc = sv[w][t] + band;
           float p = fast_exp2(fmaf(sc, sl2, -l2));
+          // (computed in every lane, then selected: kept out of branches)
+          asm volatile("" : "+v"(p));
           const bool ok = iok && j >= 0 && j < N && dlt >= dmin && dlt <= N - 1;
           p = ok ? p : 0.f;
           zd[w][t] = p * (pv[w][t] - dd);  // G' in place
