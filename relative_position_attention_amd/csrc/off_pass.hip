@@ -58,10 +58,24 @@ __device__ __forceinline__ int block_order(int k, int nob, int center) {
 template <bool CAUSAL, bool U>
 __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, float* p2, int nob,
                                                       int BH, int nchunk) {
-  // per wave: [0, 16 kOP) scratch, then the query tile (bf16) and the keys'
-  // u . k entries (128); after the loop the same memory holds the wave's
-  // partial
-  __shared__ __attribute__((aligned(16))) float sred[4][64 * 64];
+  // During the loop: the step's K and V rectangle (128 keys, shared by the
+  // four waves) and its keys' u . k entries, and per wave a scratch and its
+  // query tile (fp16 words).  After the loop the same memory holds the four
+  // waves' partials.
+  constexpr int kWave = 16 * kOP + 16 * kOQP / 2;  // floats per wave
+  struct Loop {
+    bf16 sk[128 * kOQP];
+    bf16 sv[128 * kOQP];
+    bf16 sa[64 * kOQP];  // the block's table rows s0 .. s0 + 63
+    float sbt[64];       // and their expanded bias
+    float skm[128];
+    float w[4][kWave];
+  };
+  union Mem {
+    Loop l;
+    float red[4][64 * 64];
+  };
+  __shared__ __attribute__((aligned(16))) Mem mem;
   __shared__ float sdb[4][64];
 
   const int tid = threadIdx.x;
@@ -90,9 +104,8 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
   const Rsrc rkm = make_rsrc(a.keymid + tok, row_bytes);
   const ItTables itb = it_tables(a, h);
 
-  float* const scr = &sred[wave][0];
-  bf16* const sq = reinterpret_cast<bf16*>(&sred[wave][16 * kOP]);
-  float* const skm = &sred[wave][16 * kOP + 16 * kOQP / 2];
+  float* const scr = &mem.l.w[wave][0];
+  bf16* const sq = reinterpret_cast<bf16*>(&mem.l.w[wave][16 * kOP]);
 
   floatx4 acc[4][4];
 #pragma unroll
@@ -102,137 +115,205 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
   float dbs[4] = {0.f, 0.f, 0.f, 0.f};
 
   if (dlo <= dhi) {
+    // the block's table rows s0 .. s0 + 63 (A operand of the relation
+    // entries) and their expanded bias, the same for every step: into LDS
+    // once (written before the first step's barrier)
+    {
+      const int r = tid >> 2, ch = (tid & 3) * 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<uint4*>(&mem.l.sa[r * kOQP + ch + 8 * u]) =
+            bload16(itb.at, static_cast<uint32_t>((s0 + r) * 64 + ch + 8 * u) * 2);
+      if (tid < 64) mem.l.sbt[tid] = bloadf(itb.bt, static_cast<uint32_t>(s0 + tid) * 4);
+    }
+
     // queries with a pair in the block: i in [max(0, dlo), min(N - 1, N - 1 + dhi)]
     const int i_lo = imax(0, dlo), i_hi = imin(N - 1, N - 1 + dhi);
-    for (int ib = i_lo & ~63; ib <= i_hi; ib += 64) {
-      const int qw = ib + 16 * wave;
-      if (qw > i_hi || qw + 15 < i_lo) continue;  // (uniform per wave; no barrier in the loop)
-      const int i = qw + c16;
-      const int jb = qw - dl0 - 63;
-      // Every load of the step is issued here, unconditionally (range-checked
-      // buffer loads), the per-token values first: loads complete in order,
-      // so the waits for the early ones leave the row loads in flight.
-      const float lse_i = bloadf(rlse, static_cast<uint32_t>(i) * 4);
-      const float dd_i = bloadf(rdd, static_cast<uint32_t>(i) * 4);
-      float km1 = 0.f, km2 = 0.f;
-      if (U) {
-        const int j1 = jb + lane, j2 = jb + 64 + lane;
-        km1 = bloadf(rkm, j1 >= 0 ? static_cast<uint32_t>(j1) * 4 : kOob);
-        km2 = bloadf(rkm, j2 >= 0 ? static_cast<uint32_t>(j2) * 4 : kOob);
+    // Step at ib: the workgroup's 64 queries ib .. ib + 63 (wave w: 16 from
+    // ib + 16 w) and keys jw = ib - dl0 - 63 .. jw + 127 (wave w's 80-key
+    // rectangle starts at row 16 w).  Tile staging: K and V rows (t >> 3) and
+    // 32 + (t >> 3) (+ 64, + 96), chunk t & 7; the keys' u . k by threads < 128.
+    const int kr = tid >> 3, kc8 = (tid & 7) * 8;
+    uint4 tk[4], tv[4];
+    float tkm = 0.f;
+    auto load_tile = [&](int ib) {
+      const int jw = ib - dl0 - 63;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jw + kr + 32 * u;
+        const uint32_t off = j >= 0 ? static_cast<uint32_t>(j * 128 + kc8 * 2) : kOob;
+        tk[u] = bload16(rk, off);
+        tv[u] = bload16(rv, off);
       }
-      bf16x8 qf[2], df[2];
+      if (U) {
+        const int j = jw + (tid & 127);
+        tkm = bloadf(rkm, j >= 0 ? static_cast<uint32_t>(j) * 4 : kOob);
+      }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        *reinterpret_cast<uint4*>(&mem.l.sk[(kr + 32 * u) * kOQP + kc8]) = tk[u];
+        *reinterpret_cast<uint4*>(&mem.l.sv[(kr + 32 * u) * kOQP + kc8]) = tv[u];
+      }
+      if (U && tid < 128) mem.l.skm[tid] = tkm;
+    };
+    // the wave's queries of a step: Q, dO fragments, L and D
+    bf16x8 qf[2], df[2], qn[2], dn[2];
+    float lse_i, dd_i, lse_n, dd_n;
+    auto load_queries = [&](int ib, bf16x8 (&q2)[2], bf16x8 (&d2)[2], float& ls, float& dv) {
+      const int i = ib + 16 * wave + c16;
+      ls = bloadf(rlse, static_cast<uint32_t>(i) * 4);
+      dv = bloadf(rdd, static_cast<uint32_t>(i) * 4);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint32_t off = static_cast<uint32_t>(i * 128 + 64 * c + 16 * g);
-        qf[c] = __builtin_bit_cast(bf16x8, bload16(rq, off));
-        df[c] = __builtin_bit_cast(bf16x8, bload16(rdo, off));
+        q2[c] = __builtin_bit_cast(bf16x8, bload16(rq, off));
+        d2[c] = __builtin_bit_cast(bf16x8, bload16(rdo, off));
       }
-      const bool iok = i < N;
-      const float l2 = iok ? lse_i * kLog2e : INFINITY;
-      const float dd = dd_i;
+    };
 
-      // S and dP over the 80-key rectangle (keys jb + 16 kb + 4 g + t)
-      floatx4 sr[5], pr[5];
-#pragma unroll
-      for (int kb = 0; kb < 5; ++kb) {
-        sr[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        pr[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int ib0 = i_lo & ~63;
+    load_queries(ib0, qf, df, lse_i, dd_i);
+    load_tile(ib0);
+    store_tile();
+    __syncthreads();
+    for (int ib = ib0; ib <= i_hi; ib += 64) {
+      const bool more = ib + 64 <= i_hi;
+      if (more) {
+        load_queries(ib + 64, qn, dn, lse_n, dd_n);
+        load_tile(ib + 64);
       }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
+      const int qw = ib + 16 * wave;
+      // (uniform per wave: a wave without a query in the range computes
+      // nothing but still meets the barriers)
+      if (!(qw > i_hi || qw + 15 < i_lo)) {
+        const int i = qw + c16;
+        const bool iok = i < N;
+        const float l2 = iok ? lse_i * kLog2e : INFINITY;
+        const float dd = dd_i;
+        const bf16* Ks = mem.l.sk + (16 * wave) * kOQP;
+        const bf16* Vs = mem.l.sv + (16 * wave) * kOQP;
+
+        // S and dP over the wave's 80-key rectangle (keys jb + 16 kb + 4 g
+        // + t, jb = qw - dl0 - 63)
+        floatx4 sr[5], pr[5];
 #pragma unroll
         for (int kb = 0; kb < 5; ++kb) {
-          const int j = jb + 16 * kb + c16;
-          const uint32_t off = j >= 0 ? static_cast<uint32_t>(j * 128 + 64 * c + 16 * g) : kOob;
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, bload16(rk, off));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, bload16(rv, off));
-          sr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sr[kb], 0, 0, 0);
-          pr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[c], pr[kb], 0, 0, 0);
+          sr[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          pr[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-      // relation entries of the block's rows (lane: query c16, offsets
-      // 16 w + 4 g + t)
-      floatx4 zd[4];
-      it_rows<4>(itb, s0, qf[0], qf[1], c16, g, zd);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int kb = 0; kb < 5; ++kb) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kOQP + 32 * c + 8 * g);
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (16 * kb + c16) * kOQP + 32 * c + 8 * g);
+            sr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sr[kb], 0, 0, 0);
+            pr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[c], pr[kb], 0, 0, 0);
+          }
+        // relation entries of the block's rows (lane: query c16, offsets
+        // 16 w + 4 g + t): bt, then the two K-steps, as in every pass
+        floatx4 zd[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) zd[w] = *reinterpret_cast<const floatx4*>(&mem.l.sbt[16 * w + 4 * g]);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(&mem.l.sa[(16 * w + c16) * kOQP + 32 * c + 8 * g]);
+            zd[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[c], zd[w], 0, 0, 0);
+          }
 
-      // the query tile (as fp16 words) and the keys' u . k entries for the
-      // transposing reads
+        // the query tile as fp16 words for the transposing reads
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        *reinterpret_cast<uint4*>(sq + c16 * kOQP + 32 * c + 8 * g) =
-            bf16x8_to_f16x8(__builtin_bit_cast(uint4, qf[c]));
-      if (U) {
-        // keys jb .. jb + 127 (the rectangle uses the first 80)
-        skm[lane] = km1;
-        skm[64 + lane] = km2;
-      }
+        for (int c = 0; c < 2; ++c)
+          *reinterpret_cast<uint4*>(sq + c16 * kOQP + 32 * c + 8 * g) =
+              bf16x8_to_f16x8(__builtin_bit_cast(uint4, qf[c]));
 
-      // rectangle -> (query, offset): offset 16 w + 4 g + t of query c16 is
-      // key kk = c16 + 63 - 16 w - 4 g - t
-      float sv[4][4], pv[4][4];
+        // rectangle -> (query, offset): offset 16 w + 4 g + t of query c16 is
+        // key kk = c16 + 63 - 16 w - 4 g - t
+        float sv[4][4], pv[4][4];
 #pragma unroll
-      for (int kb = 0; kb < 5; ++kb) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * kb + 4 * g) = sr[kb];
+        for (int kb = 0; kb < 5; ++kb) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * kb + 4 * g) = sr[kb];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float* r = scr + c16 * kOP + c16 + 60 - 16 * w - 4 * g;
+        for (int w = 0; w < 4; ++w) {
+          const float* r = scr + c16 * kOP + c16 + 60 - 16 * w - 4 * g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) sv[w][t] = r[3 - t];
-      }
+          for (int t = 0; t < 4; ++t) sv[w][t] = r[3 - t];
+        }
 #pragma unroll
-      for (int kb = 0; kb < 5; ++kb) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * kb + 4 * g) = pr[kb];
+        for (int kb = 0; kb < 5; ++kb) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * kb + 4 * g) = pr[kb];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float* r = scr + c16 * kOP + c16 + 60 - 16 * w - 4 * g;
+        for (int w = 0; w < 4; ++w) {
+          const float* r = scr + c16 * kOP + c16 + 60 - 16 * w - 4 * g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) pv[w][t] = r[3 - t];
-      }
-
-      // P and G' = P (dP - D) per pair (query i, offset dl0 + 16 w + 4 g + t)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int dlt = dl0 + 16 * w + 4 * g + t;
-          const int j = i - dlt;
-          float km = 0.f;
-          if (U) km = skm[c16 + 63 - 16 * w - 4 * g - t];
-          const float band = km + zd[w][t];
-          const float sc = sv[w][t] + band;
-          float p = fast_exp2(fmaf(sc, sl2, -l2));
-          // (computed in every lane, then selected: kept out of branches)
-          asm volatile("" : "+v"(p));
-          const bool ok = iok && j >= 0 && j < N && dlt >= dmin && dlt <= N - 1;
-          p = ok ? p : 0.f;
-          zd[w][t] = p * (pv[w][t] - dd);  // G' in place
+          for (int t = 0; t < 4; ++t) pv[w][t] = r[3 - t];
         }
 
-      // G'^T through the scratch: lane (c16, g) of row block w takes
-      // G'[query 4 g + e][offset 16 w + c16], e = 0..3
+        // P and G' = P (dP - D) per pair (query i, offset dl0 + 16 w + 4 g + t)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * w + 4 * g) = zd[w];
-      halfx4 ga[4];
+        for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float x[4];
+          for (int t = 0; t < 4; ++t) {
+            const int dlt = dl0 + 16 * w + 4 * g + t;
+            const int j = i - dlt;
+            float km = 0.f;
+            if (U) km = mem.l.skm[16 * wave + c16 + 63 - 16 * w - 4 * g - t];
+            const float band = km + zd[w][t];
+            const float sc = sv[w][t] + band;
+            float p = fast_exp2(fmaf(sc, sl2, -l2));
+            // (computed in every lane, then selected: kept out of branches)
+            asm volatile("" : "+v"(p));
+            const bool ok = iok && j >= 0 && j < N && dlt >= dmin && dlt <= N - 1;
+            p = ok ? p : 0.f;
+            zd[w][t] = p * (pv[w][t] - dd);  // G' in place
+          }
+
+        // G'^T through the scratch: lane (c16, g) of row block w takes
+        // G'[query 4 g + e][offset 16 w + c16], e = 0..3
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = scr[(4 * g + e) * kOP + 16 * w + c16];
-        dbs[w] += (x[0] + x[1]) + (x[2] + x[3]);
-        halfx4 v;
+        for (int w = 0; w < 4; ++w) *reinterpret_cast<floatx4*>(scr + c16 * kOP + 16 * w + 4 * g) = zd[w];
+        halfx4 ga[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(x[e]);
-        ga[w] = v;
+        for (int w = 0; w < 4; ++w) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = scr[(4 * g + e) * kOP + 16 * w + c16];
+          dbs[w] += (x[0] + x[1]) + (x[2] + x[3]);
+          halfx4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<_Float16>(x[e]);
+          ga[w] = v;
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          // Q^T: lane (c16, g) takes q[query 4 g + e][16 db + c16]
+          const halfx4 qt = __builtin_bit_cast(halfx4, lds_tr4(sq, kOQP, 4 * g, 16 * db, c16));
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            acc[w][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(ga[w], qt, acc[w][db], 0, 0, 0);
+        }
       }
+      // every wave is done with this step's rectangle: the next one goes in
+      __syncthreads();
+      if (more) {
+        store_tile();
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        // Q^T: lane (c16, g) takes q[query 4 g + e][16 db + c16]
-        const halfx4 qt = __builtin_bit_cast(halfx4, lds_tr4(sq, kOQP, 4 * g, 16 * db, c16));
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[w][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(ga[w], qt, acc[w][db], 0, 0, 0);
+        for (int c = 0; c < 2; ++c) {
+          qf[c] = qn[c];
+          df[c] = dn[c];
+        }
+        lse_i = lse_n;
+        dd_i = dd_n;
       }
+      __syncthreads();
     }
   }
 
   // the waves' partials, added in a fixed order (wave 0 + 1 + 2 + 3); tau
-  // (G = tau G') multiplies the finished sums
+  // (G = tau G') multiplies the finished sums.  (The loop's last barrier
+  // leaves the memory free.)
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const float dsum = wave_sum_g(dbs[w]);
@@ -240,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) sred[wave][(16 * w + 4 * g + t) * 64 + 16 * db + c16] = acc[w][db][t];
+      for (int t = 0; t < 4; ++t) mem.red[wave][(16 * w + 4 * g + t) * 64 + 16 * db + c16] = acc[w][db][t];
   }
   __syncthreads();
   const int64_t pbase = (static_cast<int64_t>(h) * nchunk + b) * S + s0;
@@ -249,7 +330,8 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
     const int e = tid + 256 * k;
     const int r = e >> 6;
     if (s0 + r < S)
-      p1[(pbase + r) * 64 + (e & 63)] = a.scale * (((sred[0][e] + sred[1][e]) + sred[2][e]) + sred[3][e]);
+      p1[(pbase + r) * 64 + (e & 63)] =
+          a.scale * (((mem.red[0][e] + mem.red[1][e]) + mem.red[2][e]) + mem.red[3][e]);
   }
   if (tid < 64 && s0 + tid < S)
     p2[pbase + tid] = a.scale * (((sdb[0][tid] + sdb[1][tid]) + sdb[2][tid]) + sdb[3][tid]);
