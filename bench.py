@@ -340,18 +340,23 @@ def extras(torch, rpa, synth, flush, steps=5, warmup=2):
                             warmup, flush))
     out.append(time_variant("recomputed projections", spec0, arr0, torch, rpa, False, steps,
                             warmup, flush, retain=False))
-    # In-tile relation products ([RPA] §6, Table 7 row "Projections"): the
-    # Transformer-XL shapes (identity map: stored projections are quadratic)
-    # with stored and with in-tile products
-    it_rows = []
+    return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out,
+            "in_tile_rows": in_tile_rows(torch, rpa, synth, flush, steps, warmup)}
+
+
+def in_tile_rows(torch, rpa, synth, flush, steps=5, warmup=2):
+    """In-tile relation products ([RPA] §6, Table 7 row "Projections"): the
+    Transformer-XL shapes (identity map: stored projections are quadratic)
+    with stored and with in-tile products, time and peak MiB of each."""
+    rows = []
     for label, spec_arr in (("txl B1 H8 N8192 causal", synth.make_bench("txl")),
                             ("txl B1 H8 N16384 non-causal", synth.make_config(5))):
         spec, arr = spec_arr
-        it_rows.append(time_variant(label + ", stored", spec, arr, torch, rpa, False, steps, warmup,
-                                    flush))
-        it_rows.append(time_variant(label + ", in-tile", dict(spec, in_tile=True), arr, torch, rpa,
-                                    False, steps, warmup, flush))
-    return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out, "in_tile_rows": it_rows}
+        rows.append(time_variant(label + ", stored", spec, arr, torch, rpa, False, steps, warmup,
+                                 flush))
+        rows.append(time_variant(label + ", in-tile", dict(spec, in_tile=True), arr, torch, rpa,
+                                 False, steps, warmup, flush))
+    return rows
 
 
 def cpu_baseline(mechs):
@@ -502,6 +507,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip amd-smi (e.g. under a profiler that preloads into child programs)")
+    ap.add_argument("--in-tile-only", action="store_true",
+                    help="time only the in-tile rows (stored vs in-tile products at the "
+                         "Transformer-XL shapes) and print them as one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this library has no "
@@ -520,6 +528,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rpa.library()  # fails loudly if the HIP library is missing
+    if args.in_tile_only:
+        flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda")
+        rows = in_tile_rows(torch, rpa, synth, flush, max(1, args.steps), args.warmup)
+        print(json.dumps({"in_tile_rows": rows, "steps": args.steps, "warmup": args.warmup}))
+        return
     mechs = [m for m in args.mechs.split(",") if m]
     runs = [MechRun(m, torch, rpa, synth) for m in mechs]
     stream = torch.cuda.current_stream()
