@@ -150,10 +150,12 @@ typedef struct relpos_desc {
      Projection memory and workspace become O(N) per (batch, head) slice
      (identity maps such as Transformer-XL's otherwise store O(N^2)), at the
      cost of the per-tile products.  Requires bf16 inputs and the A^Q term;
-     u, v and a scalar bias may be present; A^K, segment masks and dropout
-     are not supported with it (RELPOS_E_UNSUPPORTED).  relpos_project then
-     stores only the per-token entries and the expanded bias, and the
-     relpos_sizes figures shrink accordingly. */
+     u, v, a scalar bias, segment masks and dropout may be present; the A^K
+     term, and split_operands together with segment masks or dropout, are
+     not supported with it (RELPOS_E_UNSUPPORTED).  relpos_project then
+     stores only the per-token entries, the expanded bias and the expanded
+     table (with its transpose), and the relpos_sizes figures shrink
+     accordingly. */
   int32_t in_tile;
   int32_t reserved0;       /* must be 0                                      */
 } relpos_desc;

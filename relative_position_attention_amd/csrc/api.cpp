@@ -638,7 +638,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   // reductions read every entry a token's offsets reach, so the buffer is
   // cleared before each pass (a fill kernel; the passes write the rest)
   const size_t dz_bytes = static_cast<size_t>(p.BH) * a.dz_bh * p.dz_entry;
-  if (p.segmented && (p.need_qside || p.ak)) RP_HIP(launch_zero(dz, dz_bytes, s));
+  if (p.segmented && !p.in_tile && (p.need_qside || p.ak)) RP_HIP(launch_zero(dz, dz_bytes, s));
 
   // Query-parallel pass, then the query reduction ([RPA] Table 9)
   // (in-tile products: the query pass adds the relation part of dQ itself and
@@ -679,7 +679,7 @@ int run_bwd(const relpos_desc* desc, const relpos_shape* shape, const relpos_ten
   }
   if (p.need_qside) {
     if (p.in_tile) {
-      RP_HIP(launch_offset_pass_it(a, p.B, p.causal, p.u, p1, p2, s));
+      RP_HIP(launch_offset_pass_it(a, p.B, p.causal, p.u, p.segmented || p.drop_p8 > 0, p1, p2, s));
     } else {
       PartialArgs pa;
       pa.dz = dz;

@@ -96,10 +96,13 @@ hipError_t launch_attn_fwd_bf16_drop(int flags, const AttnArgs& a, int B, hipStr
 hipError_t launch_attn_fwd_bf16_it(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16_it(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_q_bf16_it(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_attn_fwd_bf16_it_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_q_bf16_it_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
+hipError_t launch_bwd_k_bf16_it_ext(int flags, const AttnArgs& a, int B, hipStream_t s);
 // offset-parallel pass (off_pass.hip): chunk partials P1 [H, B, S, 64] and
 // P2 [H, B, S] of the table- and bias-gradient fold, one chunk per batch row
-hipError_t launch_offset_pass_it(const AttnArgs& a, int B, int causal, int u, float* p1, float* p2,
-                                 hipStream_t s);
+hipError_t launch_offset_pass_it(const AttnArgs& a, int B, int causal, int u, int ext, float* p1,
+                                 float* p2, hipStream_t s);
 hipError_t launch_bwd_q_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_bwd_k_bf16_drop(int flags, const AttnArgs& a, int B, hipStream_t s);
 

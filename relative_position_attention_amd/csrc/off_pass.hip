@@ -32,7 +32,12 @@
 // significant bits instead of bf16's 8 (a clipped map folds thousands of
 // offsets into its edge rows, whose sums would otherwise carry the larger
 // rounding), and the bf16 queries convert to fp16 exactly.
+// EXT adds segment masks (a pair outside its query's segment is masked) and
+// dropout (dP takes the pair's keep factor, as in the query pass, applied in
+// the rectangle order, whose key runs start on multiples of 4), as defined in
+// extras.hpp.
 #include "common.hpp"
+#include "extras.hpp"
 #include "intile.hpp"
 #include "kernels.hpp"
 
@@ -55,7 +60,7 @@ __device__ __forceinline__ int block_order(int k, int nob, int center) {
   return right > left ? center + both + r : center - 1 - both - r;
 }
 
-template <bool CAUSAL, bool U>
+template <bool CAUSAL, bool U, bool EXT>
 __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, float* p2, int nob,
                                                       int BH, int nchunk) {
   // During the loop: the step's K and V rectangle (128 keys, shared by the
@@ -91,6 +96,9 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
   const int dmin = CAUSAL ? 0 : -(N - 1);
   const int dlo = imax(dl0, dmin), dhi = imin(dl0 + 63, N - 1);
   const float sl2 = a.scale_log2;
+  const bool SEG = EXT && a.seg != nullptr;
+  const bool DROP = EXT && a.drop_p8 > 0;
+  const int64_t brow = static_cast<int64_t>(b) * N;
 
   const uint64_t slice_bytes = static_cast<uint64_t>(N) * 128;
   const Rsrc rq = make_rsrc(reinterpret_cast<const bf16*>(a.q) + tok * 64, slice_bytes);
@@ -190,8 +198,15 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
       if (!(qw > i_hi || qw + 15 < i_lo)) {
         const int i = qw + c16;
         const bool iok = i < N;
-        const float l2 = iok ? lse_i * kLog2e : INFINITY;
+        float l2 = iok ? lse_i * kLog2e : INFINITY;
+        if (EXT && !(l2 > -INFINITY)) l2 = INFINITY;  // a row with no key: P = 0
         const float dd = dd_i;
+        // the query's segment (keys outside it are masked)
+        int sgl = 0, sgh = N;
+        if (SEG) {
+          sgl = sgh = 0;
+          if (iok) token_segment(a, brow, i, sgl, sgh);
+        }
         const bf16* Ks = mem.l.sk + (16 * wave) * kOQP;
         const bf16* Vs = mem.l.sv + (16 * wave) * kOQP;
 
@@ -212,6 +227,18 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
             sr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sr[kb], 0, 0, 0);
             pr[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[c], pr[kb], 0, 0, 0);
           }
+        if (DROP) {
+          // dP of a dropped pair is 0, of a kept one times the keep scale;
+          // the rectangle's keys jb + 16 kb + 4 g (+ 0..3) start on a multiple
+          // of 4 (jb = qw - dl0 - 63 is a multiple of 16)
+#pragma unroll
+          for (int kb = 0; kb < 5; ++kb) {
+            float mk[4];
+            keep_row4(a, bh, i, qw - dl0 - 63 + 16 * kb + 4 * g, a.drop_scale, mk);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) pr[kb][t] *= mk[t];
+          }
+        }
         // relation entries of the block's rows (lane: query c16, offsets
         // 16 w + 4 g + t): bt, then the two K-steps, as in every pass
         floatx4 zd[4];
@@ -265,7 +292,8 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
             float p = fast_exp2(fmaf(sc, sl2, -l2));
             // (computed in every lane, then selected: kept out of branches)
             asm volatile("" : "+v"(p));
-            const bool ok = iok && j >= 0 && j < N && dlt >= dmin && dlt <= N - 1;
+            const bool ok = iok && j >= 0 && j < N && dlt >= dmin && dlt <= N - 1 &&
+                            (!SEG || (j >= sgl && j < sgh));
             p = ok ? p : 0.f;
             zd[w][t] = p * (pv[w][t] - dd);  // G' in place
           }
@@ -339,23 +367,22 @@ __global__ __launch_bounds__(256, 2) void offset_pass(AttnArgs a, float* p1, flo
 
 }  // namespace
 
-hipError_t launch_offset_pass_it(const AttnArgs& a, int B, int causal, int u, float* p1, float* p2,
-                                 hipStream_t s) {
+template <bool C, bool U>
+hipError_t launch_op(const AttnArgs& a, int B, int ext, float* p1, float* p2, hipStream_t s) {
   const int BH = B * a.H;
   const int nob = (a.S + 63) / 64;
   const dim3 grid(static_cast<unsigned>(nob * BH));
-  if (causal) {
-    if (u)
-      hipLaunchKernelGGL((offset_pass<true, true>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
-    else
-      hipLaunchKernelGGL((offset_pass<true, false>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
-  } else {
-    if (u)
-      hipLaunchKernelGGL((offset_pass<false, true>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
-    else
-      hipLaunchKernelGGL((offset_pass<false, false>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
-  }
+  if (ext)
+    hipLaunchKernelGGL((offset_pass<C, U, true>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
+  else
+    hipLaunchKernelGGL((offset_pass<C, U, false>), grid, dim3(256), 0, s, a, p1, p2, nob, BH, B);
   return hipGetLastError();
+}
+
+hipError_t launch_offset_pass_it(const AttnArgs& a, int B, int causal, int u, int ext, float* p1,
+                                 float* p2, hipStream_t s) {
+  if (causal) return u ? launch_op<true, true>(a, B, ext, p1, p2, s) : launch_op<true, false>(a, B, ext, p1, p2, s);
+  return u ? launch_op<false, true>(a, B, ext, p1, p2, s) : launch_op<false, false>(a, B, ext, p1, p2, s);
 }
 
 }  // namespace relpos

@@ -327,8 +327,8 @@ int make_plan(const relpos_desc* desc, const relpos_shape* shape, Plan& p,
       why = "in_tile needs the A^Q term (a scalar bias alone has no projections)";
     else if (desc->terms & RELPOS_TERM_AK)
       why = "in_tile does not support the A^K term";
-    else if (desc->segmented || desc->dropout_p8 > 0)
-      why = "in_tile does not support segment masks or dropout";
+    else if (desc->split_operands && (desc->segmented || desc->dropout_p8 > 0))
+      why = "in_tile with segment masks or dropout does not support split_operands";
     if (why != nullptr) {
       detail = why;
       return RELPOS_E_UNSUPPORTED;

@@ -240,5 +240,7 @@ def test_in_tile_validation():
     assert _err(dict(t5, in_tile=True)) == -2
     deb = _spec_small(3, 300)                                       # A^K
     assert _err(dict(deb, in_tile=True)) == -2
-    assert _err(dict(txl, in_tile=True, segments=[[(0, 300)]])) == -2
-    assert _err(dict(txl, in_tile=True, dropout={"p8": 10, "seed": 1})) == -2
+    # masks and dropout compose with in-tile products, split operands with them do not
+    rpa.Problem(dict(txl, in_tile=True, segments=[[(0, 300)]])).sizes()
+    rpa.Problem(dict(txl, in_tile=True, dropout={"p8": 10, "seed": 1})).sizes()
+    assert _err(dict(txl, in_tile=True, segments=[[(0, 300)]]), split_operands=1) == -2

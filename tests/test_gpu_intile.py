@@ -111,6 +111,57 @@ def test_intile_matches_stored_projections():
     assert float(np.max(np.abs(l1 - l0))) < 2e-2
 
 
+LAYOUTS = {
+    # packed sequences in both rows, the second row ending in padding
+    "packed": [[(0, 150), (150, 420), (420, 700)], [(0, 333), (333, 690)]],
+    # padding masks: 300 and 700 valid tokens
+    "padded": [[(0, 300)], [(0, 700)]],
+    # short sequences and gaps of padding between them
+    "gaps": [[(5, 40), (64, 65), (100, 260), (400, 641)], [(0, 17), (17, 600)]],
+}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["txl", "shaw"])
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_intile_segments(layout, kind, causal):
+    # in-tile products with segment masks ([RPA] appendix "Masks, packing,
+    # and dropout"): padding rows O = 0, L = -inf; everything against the
+    # oracle
+    spec, arr = _problem(kind, causal, 101)
+    spec["segments"] = LAYOUTS[layout]
+    label = f"intile-seg-{layout}-{kind}-c{int(causal)}"
+    print(f"[intile] {label}", flush=True)
+    got = run_library(spec, arr)
+    check(spec, got, oracle.forward_backward(spec, arr), label=label)
+    for b, segs in enumerate(spec["segments"]):
+        pad = np.ones(spec["N"], bool)
+        for s0, s1 in segs:
+            pad[s0:s1] = False
+        assert np.all(got["o"][b][:, pad] == 0)
+        assert np.all(np.isneginf(got["lse"][b][:, pad]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["txl", "shaw"])
+def test_intile_dropout(kind, causal):
+    spec, arr = _problem(kind, causal, 103)
+    spec["dropout"] = {"p8": 26, "seed": 0x5EED0000 + 11 * len(kind)}
+    label = f"intile-drop-{kind}-c{int(causal)}"
+    print(f"[intile] {label}", flush=True)
+    check(spec, run_library(spec, arr), oracle.forward_backward(spec, arr), label=label)
+
+
+@pytest.mark.parametrize("kind", ["txl", "shaw"])
+def test_intile_segments_and_dropout(kind):
+    spec, arr = _problem(kind, False, 107)
+    spec["segments"] = LAYOUTS["packed"]
+    spec["dropout"] = {"p8": 77, "seed": 0x0123456789ABCDEF}
+    label = f"intile-seg+drop-{kind}"
+    print(f"[intile] {label}", flush=True)
+    check(spec, run_library(spec, arr), oracle.forward_backward(spec, arr), label=label)
+
+
 def test_intile_rejects_key_table():
     spec, arr = make_problem(kind="deberta", B=1, H=2, N=200, dtype="bf16", seed=3, causal=False,
                              d_model=128)
