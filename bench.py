@@ -230,7 +230,8 @@ def visible_pairs(spec):
     return tot
 
 
-def time_variant(label, spec, arr, torch, rpa, split, steps, warmup, flush, retain=True):
+def time_variant(label, spec, arr, torch, rpa, split, steps, warmup, flush, retain=True,
+                 out_dtype="f32"):
     """Forward (projection + attention, or attention alone recomputing the
     projections) and backward of one problem variant, median ms over `steps`
     flushed samples, with credited TFLOP/s over its visible pairs and the
@@ -240,7 +241,7 @@ def time_variant(label, spec, arr, torch, rpa, split, steps, warmup, flush, reta
     if spec.get("segments") is not None:
         t["seg"] = torch.from_numpy(rpa.segment_bounds(spec["segments"], spec["B"],
                                                        spec["N"])).cuda()
-    prob = rpa.Problem(spec, out_dtype="f32", split_operands=split)
+    prob = rpa.Problem(spec, out_dtype=out_dtype, split_operands=split)
     B, H, N, d = spec["B"], spec["H"], spec["N"], spec["d"]
     pairs = visible_pairs(spec) * H
     nproj = sum(1 for x in ("aq", "ak") if x in spec["terms"])
@@ -251,7 +252,8 @@ def time_variant(label, spec, arr, torch, rpa, split, steps, warmup, flush, reta
                        dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(max(sz["bwd_ws_bytes"] if retain else sz["bwd_ws_bytes_noz"], 256),
                        dtype=torch.uint8, device="cuda")
-    o = torch.empty((B, H, N, 64), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, N, 64), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                    device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     grads = rpa.empty_grads(prob, torch.device("cuda"))
     stream = torch.cuda.current_stream()
@@ -316,8 +318,9 @@ def extras(torch, rpa, synth, flush, steps=5, warmup=2):
     sequences (four documents of 2048 tokens per row, segment mask),
     padding (row lengths 8192 and 5000), attention dropout (26/256), a map
     whose rows are not contiguous offset intervals (|delta| clipped at 256,
-    delta and -delta sharing a row), and projections recomputed in both
-    passes instead of retained.  Credited FLOPs count visible pairs."""
+    delta and -delta sharing a row), projections recomputed in both
+    passes instead of retained, and bf16 outputs.  Credited FLOPs count
+    visible pairs."""
     import copy
     spec0, arr0 = synth.make_bench("shaw")
     out = []
@@ -340,6 +343,8 @@ def extras(torch, rpa, synth, flush, steps=5, warmup=2):
                             warmup, flush))
     out.append(time_variant("recomputed projections", spec0, arr0, torch, rpa, False, steps,
                             warmup, flush, retain=False))
+    out.append(time_variant("bf16 outputs (O, dQ, dK, dV)", spec0, arr0, torch, rpa, False, steps,
+                            warmup, flush, out_dtype="bf16"))
     return {"shape": "shaw B2 H12 N8192 clip 256, bf16", "rows": out,
             "in_tile_rows": in_tile_rows(torch, rpa, synth, flush, steps, warmup)}
 
