@@ -112,6 +112,21 @@ def cases():
     out.append(("txl-c-46000", rpa.Problem(_txl(46000, True))))
     out.append(("txl-c-47000", rpa.Problem(_txl(47000, True))))
     out.append(("id-bias-f32-24000", rpa.Problem(_txl(24000, False, "f32", ("aq", "bias")))))
+    # in-tile products: the Transformer-XL configurations, a clipped map, N = 1,
+    # past the stored path's slice limit, with masks and dropout, and refusals
+    for label, spec in (("it-cfg4", _full(CONFIGS[4])), ("it-cfg5", _full(CONFIGS[5])),
+                        ("it-shaw", scaled_config(1, B=2, H=2, N=700, dtype="bf16")[0]),
+                        ("it-txl-N1", _txl(1, False)), ("it-txl-nc-32768", _txl(32768, False)),
+                        ("it-txl-c-47000", _txl(47000, True)),
+                        ("it-seg-drop", dict(_txl(700, True), segments=[[(0, 700)]],
+                                             dropout={"p8": 9, "seed": 3})),
+                        ("it-deberta", _full(CONFIGS[3])),
+                        ("it-f32", scaled_config(1, B=1, H=2, N=128)[0])):
+        out.append((label, rpa.Problem(dict(spec, in_tile=True))))
+    out.append(("it-split-seg", _edit(rpa.Problem(dict(_txl(300, False), in_tile=True,
+                                                       segments=[[(0, 300)]])),
+                                      split_operands=1)))
+    out.append(("it-flag-2", _edit(rpa.Problem(dict(_txl(300, False), in_tile=True)), in_tile=2)))
     return out
 
 
@@ -163,6 +178,12 @@ def test_plan_under_sanitizers(tmp_path):
     assert codes["txl-nc-32000"] == 0 and codes["txl-nc-32768"] == -2
     assert codes["txl-c-46000"] == 0 and codes["txl-c-47000"] == -2
     assert codes["id-bias-f32-24000"] == -2
+    for label in ("it-cfg4", "it-cfg5", "it-shaw", "it-txl-N1", "it-txl-nc-32768",
+                  "it-txl-c-47000", "it-seg-drop"):
+        assert codes[label] == 0, label
+    for label in ("it-deberta", "it-f32", "it-split-seg"):
+        assert codes[label] == -2, label
+    assert codes["it-flag-2"] == -1
     if os.path.exists(rpa.library_path()):
         for (label, prob), line in zip(items, lines):
             assert _library_line(prob) == line, label
