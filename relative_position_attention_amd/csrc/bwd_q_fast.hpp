@@ -49,6 +49,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   constexpr bool KC = (F & (F_ZK | F_U)) != 0;
   constexpr bool KC3 = (F & F_ZK) != 0;
   constexpr bool IT = (F & F_IT) != 0;
+  // raised wave priority around the matrix products (measured at N = 8192:
+  // up to 7% faster without a key table, 2% slower with one)
+  constexpr bool PRIO = !IT && !(F & F_ZK);
   using GT = std::conditional_t<(F & F_DZ16) != 0, _Float16,
                                 typename DzType<bf16, (F & F_DZ32) != 0>::type>;
   // key projections of a band tile are staged into LDS once per workgroup
@@ -316,6 +319,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
       }
+      prio_matrix<PRIO>();
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -331,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
         }
       }
 
+      prio_normal<PRIO>();
       // relation terms (same values as the forward); off = the row's
       // constant on saturated tiles.  pure: a band tile without any pair
       // |delta| >= D (every tile of an identity map), whose selects are
@@ -560,6 +565,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       }
 
       // dQ^T += K^T G'^T
+      prio_matrix<PRIO>();
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 gf[2], gl[2];
@@ -593,6 +599,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       }
     }
 
+    prio_normal<PRIO>();
     if (kt + 1 < kt_end) store_tile(buf ^ 1);
     __syncthreads();
   }

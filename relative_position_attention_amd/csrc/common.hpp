@@ -256,6 +256,19 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
+// Wave priority around a run of matrix products (ON selects it per kernel
+// variant): a wave about to issue MFMAs is preferred by the SIMD's issue
+// arbiter, so the matrix core is fed while the SIMD's other wave runs its
+// vector work in the gaps.  It changes no result, only the issue order.
+template <bool ON>
+__device__ __forceinline__ void prio_matrix() {
+  if constexpr (ON) __builtin_amdgcn_s_setprio(1);
+}
+template <bool ON>
+__device__ __forceinline__ void prio_normal() {
+  if constexpr (ON) __builtin_amdgcn_s_setprio(0);
+}
+
 // Wait for every outstanding vector memory load of the wave (s_waitcnt
 // vmcnt(0), the other counters left free).  Used once after the loads that
 // precede a tile loop on a conditional path: without it the compiler cannot

@@ -64,6 +64,9 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
   constexpr bool SPLIT = (F & F_SPLIT) != 0;
   constexpr bool EXT = (F & (F_SEG | F_DROP)) != 0;
   constexpr bool IT = (F & F_IT) != 0;
+  // raised wave priority around the matrix products (measured at N = 8192:
+  // up to 3% faster, never slower, on the four mechanisms)
+  constexpr bool PRIO = !IT;
   // per-key relation entries: with a key table (F_ZK) the band value and the
   // two boundary values differ per key; with only the Transformer-XL u term
   // they are one value u . k_j
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
           }
         }
       }
+      prio_matrix<PRIO>();
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
         }
       }
 
+      prio_normal<PRIO>();
       // ---- relation terms: s becomes S plus the per-pair terms (score
       // units); off[qb] is the row's constant term (scaled) on saturated tiles
       float off[QB];
@@ -523,6 +528,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
       floatx4 ls[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) ls[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      prio_matrix<PRIO>();
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 pf[QB], pl[QB], pd[QB], pdl[QB];
@@ -575,6 +581,7 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
           if (SPLIT) ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kOnes8, pl[qb], ls[qb], 0, 0, 0);
         }
       }
+      prio_normal<PRIO>();
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         if (act[qb]) l[qb] += ls[qb][0];
