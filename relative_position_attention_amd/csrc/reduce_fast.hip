@@ -251,16 +251,29 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   __shared__ __attribute__((aligned(16))) int so[64];
   __shared__ __attribute__((aligned(16))) bf16 xt[64 * kRP];   // [token][d]
   __shared__ float bsh[2][64];
+  __shared__ float bred[4][2][64];  // boundary sums per token quarter
   __shared__ float p2red[4][64 * W];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int D = p.D;
   // s tiles from the one holding offset 0 (s = D) outwards: those reach the
-  // most tokens, so the longest blocks start first
+  // most tokens, so the longest blocks start first.  Workgroups are numbered
+  // rank-major (every head and chunk of one tile rank before the next rank),
+  // so the longest blocks of all heads start first, not those of the first
+  // head only (a causal map's central tiles take 32 stages per chunk where
+  // its outer ones take none: the last head's central tiles, dispatched
+  // last, ran alone at the end)
   int tile;
+  const int lin = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int nhz = static_cast<int>(gridDim.y * gridDim.z);
+  const int rank = lin / nhz, hz = lin % nhz;
   {
     const int T = static_cast<int>(gridDim.x), c = imin(D / (64 * W), T - 1);
     const int below = c, above = T - 1 - c, mm = imin(below, above);
-    const int k = static_cast<int>(blockIdx.x) - 1;
+    // the two last tiles of the centre-out order (the outermost, which hold
+    // the boundary rows 0 and 2D and so visit every token block of their
+    // chunk) move to ranks 1 and 2
+    const int r = T <= 3 ? rank : (rank == 0 ? 0 : (rank <= 2 ? T - 3 + rank : rank - 2));
+    const int k = r - 1;
     if (k < 0)
       tile = c;
     else if (k < 2 * mm)
@@ -269,8 +282,8 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
       tile = above > below ? c + mm + 1 + (k - 2 * mm) : c - mm - 1 - (k - 2 * mm);
   }
   const int s0 = tile * 64 * W;
-  const int h = blockIdx.y;
-  const int chunk = blockIdx.z;
+  const int h = hz % static_cast<int>(gridDim.y);
+  const int chunk = hz / static_cast<int>(gridDim.y);
   const int nrb = (p.N + 63) / 64;
   const int total = p.B * nrb;
   const int per = (total + p.nchunk - 1) / p.nchunk;
@@ -288,8 +301,11 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   float p2acc[W];              // thread (s = 64 st + (tid & 63), quarter tid >> 6)
 #pragma unroll
   for (int st = 0; st < W; ++st) p2acc[st] = 0.f;
-  float bx0 = 0.f, bx1 = 0.f;  // boundary P1 (threads < 64: d = tid)
-  float bs0 = 0.f, bs1 = 0.f;  // boundary P2 (every thread < 64, same order)
+  // boundary P1: thread (d = tid & 63, token quarter tid >> 6); boundary P2:
+  // thread tid < 64 sums token tid over the stages (both summed in a fixed
+  // order at the end)
+  float bx0 = 0.f, bx1 = 0.f;
+  float bs0 = 0.f, bs1 = 0.f;
 
   // does row block sb reach this block's band rows (uniform)
   auto band_hit = [&](int sb) {
@@ -404,20 +420,19 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
       }
     }
     if (has0 || has2) {
-      if (want_p1 && tid < 64) {
-        for (int tk = 0; tk < 64; ++tk) {
-          const float xv = static_cast<float>(xt[tk * kRP + tid]);
-          bx0 += bsh[0][tk] * xv;
-          bx1 += bsh[1][tk] * xv;
+      if (want_p1) {
+        const int d = tid & 63, q = tid >> 6;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int tk = 16 * q + e;
+          const float xv = static_cast<float>(xt[tk * kRP + d]);
+          bx0 = fmaf(bsh[0][tk], xv, bx0);
+          bx1 = fmaf(bsh[1][tk], xv, bx1);
         }
       }
       if (want_p2 && tid < 64) {
-        // every writer thread of P2 holds the boundary sums (the row s = 2D
-        // is written by thread 2D - s0)
-        for (int tk = 0; tk < 64; ++tk) {
-          bs0 += bsh[0][tk];
-          bs1 += bsh[1][tk];
-        }
+        bs0 += bsh[0][tid];
+        bs1 += bsh[1][tid];
       }
     }
     __syncthreads();
@@ -436,17 +451,39 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) p.p1[(pbase + s) * 64 + 16 * db + c16] = acc[st][db][t];
       }
+    if (has0 || has2) {
+      bred[tid >> 6][0][tid & 63] = bx0;
+      bred[tid >> 6][1][tid & 63] = bx1;
+    }
     __syncthreads();
-    if (tid < 64) {
+    if ((has0 || has2) && tid < 64) {
       // boundary rows: added in a fixed order after the band part
-      if (has0) p.p1[(pbase + 0) * 64 + tid] += bx0 + (2 * D == 0 ? bx1 : 0.f);
-      if (has2 && D > 0) p.p1[(pbase + 2 * D) * 64 + tid] += bx1;
+      const float t0 = ((bred[0][0][tid] + bred[1][0][tid]) + bred[2][0][tid]) + bred[3][0][tid];
+      const float t1 = ((bred[0][1][tid] + bred[1][1][tid]) + bred[2][1][tid]) + bred[3][1][tid];
+      if (has0) p.p1[(pbase + 0) * 64 + tid] += t0 + (2 * D == 0 ? t1 : 0.f);
+      if (has2 && D > 0) p.p1[(pbase + 2 * D) * 64 + tid] += t1;
     }
   }
   if (want_p2) {
 #pragma unroll
     for (int st = 0; st < W; ++st) p2red[tid >> 6][64 * st + (tid & 63)] = p2acc[st];
+    // (bred is free again: its last reads precede the P1 epilogue's writes
+    // of the partials, or it was never used)
+    if ((has0 || has2) && tid < 64) {
+      bred[0][0][tid] = bs0;
+      bred[0][1][tid] = bs1;
+    }
     __syncthreads();
+    if ((has0 || has2) && tid < 64) {
+      // every writer thread of P2 forms the same totals in the same order
+      // (the row s = 2D is written by thread 2D - s0)
+      bs0 = 0.f;
+      bs1 = 0.f;
+      for (int tk = 0; tk < 64; ++tk) {
+        bs0 += bred[0][0][tk];
+        bs1 += bred[0][1][tk];
+      }
+    }
     if (tid < 64) {
 #pragma unroll
       for (int st = 0; st < W; ++st) {
