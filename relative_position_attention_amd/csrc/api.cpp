@@ -360,7 +360,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     if (dt == 0)
       RP_HIP(launch_project_f32(pa, p.BH, max_pitch(p.zq), s));
     else
-      RP_HIP(launch_project_bf16(pa, p.BH, s));
+      RP_HIP(launch_project_bf16(pa, p.BH, max_pitch(p.zq), s));
   }
   if (p.ak) {
     ProjectArgs pa;
@@ -379,7 +379,7 @@ int project_into(const Plan& p, const relpos_desc* desc, const relpos_tensors* i
     if (dt == 0)
       RP_HIP(launch_project_f32(pa, p.BH, max_pitch(p.zk), s));
     else
-      RP_HIP(launch_project_bf16(pa, p.BH, s));
+      RP_HIP(launch_project_bf16(pa, p.BH, max_pitch(p.zk), s));
   }
   RowKeyArgs rk;
   rk.q = in->q;

@@ -175,8 +175,9 @@ struct ProjectArgs {
   int N, H, D, S, NG;
 };
 hipError_t launch_project_f32(const ProjectArgs& p, int BH, int max_pitch, hipStream_t s);
-// bf16 inputs: row-walking projection with LDS-staged table tiles
-hipError_t launch_project_bf16(const ProjectArgs& p, int BH, hipStream_t s);
+// bf16 inputs: row-walking projection with LDS-staged table tiles (rows
+// longer than 16 column tiles split over several workgroups)
+hipError_t launch_project_bf16(const ProjectArgs& p, int BH, int max_pitch, hipStream_t s);
 
 struct RowKeyArgs {
   const void* q;

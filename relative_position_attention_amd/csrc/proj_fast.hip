@@ -10,8 +10,10 @@
 // tiles of one row fill the same cache lines back to back, and the next
 // tile's 64 table rows are loaded into registers while the current tile is
 // multiplied, then put into LDS (double buffered), where the four waves read
-// them as MFMA B operands.  Workgroups are ordered widest group first, which
-// balances the jagged windows of causal identity maps.
+// them as MFMA B operands.  Rows longer than 16 tiles are split into
+// segments of equal tile counts, one workgroup each (a causal identity map's
+// last rows hold 2N/64 tiles: walked by one workgroup, they set the kernel's
+// time alone).  Workgroups are ordered widest group first.
 //
 // Stores.  A row of Z starts at an arbitrary element (rows are packed at a
 // pitch of 7 or 1 mod 8), so the results of a middle tile go through LDS:
@@ -19,8 +21,9 @@
 // threads store whole aligned 16-byte chunks (eight per row and tile instead
 // of 64 2-byte stores).  The chunk that runs into the next tile (the row's
 // last m values) is carried over in LDS and stored with the next tile's
-// first chunk.  The first and the last tile of a row store their entries one
-// by one, as does the carried part that the last tile takes over.
+// first chunk.  The first and the last tile of a row segment store their
+// entries one by one, as does the carried part that the last tile takes
+// over.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -32,17 +35,24 @@ constexpr int kTP = 72;  // LDS pitch of a table tile (bf16), 144-byte rows
 constexpr int kZT = 88;  // LDS pitch of the staged result tile (fp16): 64 + 8 + carry room
 typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
+__global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb, int nseg, int seg_tiles) {
   __shared__ __attribute__((aligned(16))) bf16 st[2][64 * kTP];
   __shared__ float sb[2][64];
   __shared__ __attribute__((aligned(16))) _Float16 zt[64 * kZT];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, c16 = lane & 15;
   const int bh = blockIdx.x;
-  const int rb = nrb - 1 - static_cast<int>(blockIdx.y);
+  const int rb = nrb - 1 - static_cast<int>(blockIdx.y) / nseg;
+  const int seg = static_cast<int>(blockIdx.y) % nseg;
   const int h = bh % p.H;
   const int r0 = rb * 64;
   const int grp = r0 / kGroup;
   const GroupInfo gi = p.gi[grp];
+  // this workgroup's column tiles: [t0, t0 + nct) of the row's tiles
+  const int t0 = seg * seg_tiles;
+  const int nct_row = (gi.pitch + 63) / 64;
+  if (t0 >= nct_row) return;
+  const int nct = imin(seg_tiles, nct_row - t0);
+  const int cb0 = 64 * t0;  // first column
   const int D2 = 2 * p.D;
   const int64_t tok = static_cast<int64_t>(bh) * p.N;
   const Rsrc rx = make_rsrc(reinterpret_cast<const bf16*>(p.x) + tok * 64,
@@ -77,10 +87,10 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   };
   TabRegs ra0, ra1;
   auto load_tab = [&](TabRegs& R, int c0) {
-    const int s = iclamp(c0 + ar - gi.pad + gi.slo, 0, D2);
+    const int s = iclamp(cb0 + c0 + ar - gi.pad + gi.slo, 0, D2);
 #pragma unroll
     for (int u = 0; u < 2; ++u) R.a[u] = bload16(ra, static_cast<uint32_t>(s * 128 + (ac + 8 * u) * 2));
-    const int sc = iclamp(c0 + (tid & 63) - gi.pad + gi.slo, 0, D2);
+    const int sc = iclamp(cb0 + c0 + (tid & 63) - gi.pad + gi.slo, 0, D2);
     R.b = bloadf(rbt, static_cast<uint32_t>(sc) * 4);
   };
   auto store_tab = [&](const TabRegs& R, int buf) {
@@ -91,7 +101,6 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
 
   const Rsrc rz = make_rsrc(reinterpret_cast<_Float16*>(p.z) + static_cast<int64_t>(bh) * p.z_bh,
                             static_cast<uint64_t>(p.z_bh) * 2);
-  const int nct = (gi.pitch + 63) / 64;
   const int g0 = grp * kGroup;
 
   // MFMA tile of columns c0 .. c0+63 (lane: rows rw + 4g + e, column 16 cb +
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
   auto store_each = [&](int c0, const float (&val)[4][4]) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int col = c0 + 16 * cb + c16;
+      const int col = cb0 + c0 + 16 * cb + c16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = rw + 4 * g + e;
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
     for (int u = 0; u < 2; ++u) {
       const int k = zq + 4 * u;
       const uint4 w = *reinterpret_cast<const uint4*>(&zt[zr * kZT + 8 * k]);
-      const uint32_t off = zi < p.N ? static_cast<uint32_t>(zstart + c0 + 8 * k) * 2 : kOob;
+      const uint32_t off = zi < p.N ? static_cast<uint32_t>(zstart + cb0 + c0 + 8 * k) * 2 : kOob;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w), rz, off, 0, 0);
     }
     if (zq == 0)
@@ -208,11 +217,9 @@ __global__ __launch_bounds__(256) void project_fast(ProjectArgs p, int nrb) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int k = zq + 4 * u;  // carried entry k of row zr (k < m)
-        const int col = t * 64 - zm + k;
         const bool ok = k < zm && zi < p.N;
-        const uint32_t off = ok ? static_cast<uint32_t>(zstart + t * 64 + k) * 2 : kOob;
+        const uint32_t off = ok ? static_cast<uint32_t>(zstart + cb0 + t * 64 + k) * 2 : kOob;
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, zt[zr * kZT + k]), rz, off, 0, 0);
-        (void)col;
       }
     }
   }
@@ -222,9 +229,14 @@ inline unsigned nblk(int64_t n, int b) { return static_cast<unsigned>((n + b - 1
 
 }  // namespace
 
-hipError_t launch_project_bf16(const ProjectArgs& p, int BH, hipStream_t s) {
+hipError_t launch_project_bf16(const ProjectArgs& p, int BH, int max_pitch, hipStream_t s) {
   const int nrb = static_cast<int>(nblk(p.N, 64));
-  hipLaunchKernelGGL(project_fast, dim3(BH, nrb), dim3(256), 0, s, p, nrb);
+  // rows of up to 16 tiles take one workgroup; longer ones split into nseg
+  // segments of seg_tiles tiles
+  const int nct_max = static_cast<int>(nblk(max_pitch, 64));
+  const int nseg = static_cast<int>(nblk(nct_max, 16));
+  const int seg_tiles = static_cast<int>(nblk(nct_max, nseg));
+  hipLaunchKernelGGL(project_fast, dim3(BH, nrb * nseg), dim3(256), 0, s, p, nrb, nseg, seg_tiles);
   return hipGetLastError();
 }
 
