@@ -52,6 +52,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   // raised wave priority around the matrix products (measured at N = 8192:
   // up to 7% faster without a key table, 2% slower with one)
   constexpr bool PRIO = !IT && !(F & F_ZK);
+  // with a key table, band terms as the initial value of the S accumulator
+  // (8% faster: see below); without one the Z^Q runs, then requested before
+  // the products, cost more than that saves
+  constexpr bool BAND_INIT = (F & F_ZK) != 0;
   using GT = std::conditional_t<(F & F_DZ16) != 0, _Float16,
                                 typename DzType<bf16, (F & F_DZ32) != 0>::type>;
   // key projections of a band tile are staged into LDS once per workgroup
@@ -308,34 +312,57 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       // the wider one), so block 1's products are always made
       const bool both = act[0];
       floatx4 s[2][4], dp[2][4];
+      // initial values: dP zero; S the key's boundary entry on saturated
+      // tiles (with per-key entries), else zero
+      auto sat_init = [&](int qb) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int kb = 0; kb < 4; ++kb) {
           floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
           if (KC && sat[qb])
             kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
           s[qb][kb] = kx;
-          dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-      }
-      prio_matrix<PRIO>();
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      };
+      if constexpr (!BAND_INIT) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kP + 32 * c + 8 * g);
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (16 * kb + c16) * kP + 32 * c + 8 * g);
-          if (both) {
-            s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][c], s[0][kb], 0, 0, 0);
-            dp[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[0][c], dp[0][kb], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (KC && sat[qb])
+              kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
+            s[qb][kb] = kx;
+            dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][c], s[1][kb], 0, 0, 0);
-          dp[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[1][c], dp[1][kb], 0, 0, 0);
         }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
+      // S^T = K Q^T and dP^T = V dO^T added to the accumulators' initial
+      // values
+      auto products = [&]() {
+        prio_matrix<PRIO>();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kP + 32 * c + 8 * g);
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + (16 * kb + c16) * kP + 32 * c + 8 * g);
+            if (both) {
+              s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][c], s[0][kb], 0, 0, 0);
+              dp[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[0][c], dp[0][kb], 0, 0, 0);
+            }
+            s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][c], s[1][kb], 0, 0, 0);
+            dp[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, df[1][c], dp[1][kb], 0, 0, 0);
+          }
+        }
+        prio_normal<PRIO>();
+      };
+      if constexpr (!BAND_INIT) products();
 
-      prio_normal<PRIO>();
       // relation terms (same values as the forward); off = the row's
       // constant on saturated tiles.  pure: a band tile without any pair
       // |delta| >= D (every tile of an identity map), whose selects are
@@ -349,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
       float off[2];
       // transposing-read address of this lane in szk (lds_tr4 with row0 = 4g)
       const _Float16* szk_lane = szk + (4 * g + (c16 >> 2)) * kZP + 4 * (c16 & 3);
-      auto band_q = [&](int qb, auto PURE) {
+      auto band_q = [&](int qb, auto PURE, auto ASSIGN) {
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
@@ -409,27 +436,62 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
             float band = km[t] + zq[t];
             if (F & F_ZK) band += static_cast<float>(zk4[t]);
             if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+            float add;
             if constexpr (PURE) {
-              s[qb][kb][t] += band;
+              add = band;
             } else {
               const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
-              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+              add = dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
             }
+            if constexpr (ASSIGN)
+              s[qb][kb][t] = add;  // the initial value of the accumulator
+            else
+              s[qb][kb][t] += add;
           }
           // keep each 4-run's loads next to their use (register pressure)
           __builtin_amdgcn_sched_barrier(0);
         }
       };
+      if constexpr (BAND_INIT) {
+        // (no causal pairing with a key table) each branch makes its own
+        // products: a band tile's terms are the accumulator's initial value,
+        // so both branches leave S in the registers of their own MFMA
+        // results (with the terms added after the products, the saturated
+        // branch copied every score into the band branch's registers)
+        if (sat[0] && sat[1]) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        off[qb] = 0.f;
-        if (!act[qb]) continue;
-        if (sat[qb])
-          off[qb] = side[qb] ? rhi[qb] : rlo[qb];
-        else if (pure[qb])
-          band_q(qb, std::true_type{});
-        else
-          band_q(qb, std::false_type{});
+          for (int qb = 0; qb < 2; ++qb) {
+            sat_init(qb);
+            off[qb] = side[qb] ? rhi[qb] : rlo[qb];
+          }
+          products();
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            off[qb] = 0.f;
+            if (sat[qb]) {
+              sat_init(qb);
+              off[qb] = side[qb] ? rhi[qb] : rlo[qb];
+            } else if (pure[qb]) {
+              band_q(qb, std::true_type{}, std::true_type{});
+            } else {
+              band_q(qb, std::false_type{}, std::true_type{});
+            }
+          }
+          products();
+        }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          off[qb] = 0.f;
+          if (!act[qb]) continue;
+          if (sat[qb])
+            off[qb] = side[qb] ? rhi[qb] : rlo[qb];
+          else if (pure[qb])
+            band_q(qb, std::true_type{}, std::false_type{});
+          else
+            band_q(qb, std::false_type{}, std::false_type{});
+        }
       }
 
       // P, then G' = P (dP - D) in place of s; tau is applied to the sums

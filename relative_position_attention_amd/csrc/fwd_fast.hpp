@@ -343,46 +343,52 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
         side[qb] = kt < n_hi[qb] ? 1 : 0;
       }
       floatx4 s[QB][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (!PAIR) {
-          floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
-          if (KC && sat[0])
-            kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[0] : 2][16 * kb + 4 * g]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = kx;
-        } else {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (KC && sat[qb])
-              kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
-            s[qb][kb] = kx;
-          }
-        }
-      }
-      prio_matrix<PRIO>();
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      // the saturated tiles' initial value of the S accumulator: the key's
+      // boundary entry (with per-key entries), else zero
+      auto sat_init = [&]() {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kKP + 32 * c + 8 * g);
+          if (!PAIR) {
+            floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (KC && sat[0])
+              kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[0] : 2][16 * kb + 4 * g]);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            if (qb == 0 && !act[0]) continue;
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = kx;
+          } else {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              floatx4 kx = floatx4{0.f, 0.f, 0.f, 0.f};
+              if (KC && sat[qb])
+                kx = *reinterpret_cast<const floatx4*>(&skc[buf][KC3 ? side[qb] : 2][16 * kb + 4 * g]);
+              s[qb][kb] = kx;
+            }
           }
         }
-      }
-
-      prio_normal<PRIO>();
+      };
+      // S^T = K Q^T added to the accumulator's initial value
+      auto products = [&]() {
+        prio_matrix<PRIO>();
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c16) * kKP + 32 * c + 8 * g);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              if (qb == 0 && !act[0]) continue;
+              s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][c], s[qb][kb], 0, 0, 0);
+            }
+          }
+        }
+        prio_normal<PRIO>();
+      };
       // ---- relation terms: s becomes S plus the per-pair terms (score
       // units); off[qb] is the row's constant term (scaled) on saturated tiles
       float off[QB];
       // band tile: per-pair terms; pairs with |delta| >= D take the boundary
       // entries (PURE: the tile holds no such pair, as every tile of an
       // identity map does, and the selects are skipped)
-      auto band_terms = [&](int qb, auto PURE) {
+      auto band_terms = [&](int qb, auto PURE, auto ASSIGN) {
         const int i = qbase[qb] + c16;
         const bool iok = i < N;
         const int zrow = giq[qb].base + (i - gq0[qb]) * giq[qb].pitch;
@@ -431,13 +437,18 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
             float band = km[t] + zq[t];
             if (F & F_ZK) band += static_cast<float>(zk4[t]);
             if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
+            float add;
             if constexpr (PURE) {
-              s[qb][kb][t] += band;
+              add = band;
             } else {
               // boundary pairs: the row's entry plus the key's
               const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
-              s[qb][kb][t] += dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+              add = dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
             }
+            if constexpr (ASSIGN)
+              s[qb][kb][t] = add;
+            else
+              s[qb][kb][t] += add;
           }
         }
       };
@@ -452,22 +463,29 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
             s[qb][kb][t] = (j >= N || (CAUSAL && j > i) || off_seg) ? -INFINITY : s[qb][kb][t];
           }
       };
-      if (!PAIR) {
-        // the wave's blocks share one region and one edge test
+      if (!PAIR && !IT) {
+        // the wave's blocks share one region and one edge test.  Each branch
+        // makes its own products: a band tile's terms are the accumulator's
+        // initial value, so both branches leave S in the registers of their
+        // own MFMA results (with the terms added after the products, the
+        // saturated branch copied every score into the band branch's
+        // registers: 3-5% slower)
         if (sat[0]) {
+          sat_init();
+          products();
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) off[qb] = (side[0] ? rhi[qb] : rlo[qb]) * sl2;
         } else {
-          // (in-tile products: every pair lies in the band)
-          const bool pure = IT || (qbase[0] - (j0 + 63) > -D && qbase[QB - 1] + 15 - j0 < D);
+          const bool pure = qbase[0] - (j0 + 63) > -D && qbase[QB - 1] + 15 - j0 < D;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             off[qb] = 0.f;
             if (pure)
-              band_terms(qb, std::true_type{});
+              band_terms(qb, std::true_type{}, std::true_type{});
             else
-              band_terms(qb, std::false_type{});
+              band_terms(qb, std::false_type{}, std::true_type{});
           }
+          products();
         }
         if ((j0 + 64 > N) || (CAUSAL && j0 + 63 > qbase[0]) ||
             (SEG && (j0 < sw.ilo || j0 + 64 > sw.ihi))) {
@@ -477,6 +495,10 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
           for (int qb = 0; qb < QB; ++qb) mask_block(qb);
         }
       } else {
+        // causal pairing (per-block regions) and in-tile products: the terms
+        // are added after the products, as in the backward passes
+        sat_init();
+        products();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           off[qb] = 0.f;
@@ -484,14 +506,20 @@ __global__ __launch_bounds__(256, ((F & F_ZK) || (F & F_CAUSAL) || (F & F_U) || 
           if (sat[qb])
             off[qb] = (side[qb] ? rhi[qb] : rlo[qb]) * sl2;
           else if (IT || (qbase[qb] - (j0 + 63) > -D && qbase[qb] + 15 - j0 < D))
-            band_terms(qb, std::true_type{});
+            band_terms(qb, std::true_type{}, std::false_type{});
           else
-            band_terms(qb, std::false_type{});
-          if ((j0 + 64 > N) || (j0 + 63 > qbase[qb]) ||
-              (SEG && (j0 < sw.ilo || j0 + 64 > sw.ihi))) {
+            band_terms(qb, std::false_type{}, std::false_type{});
+          if (PAIR && ((j0 + 64 > N) || (j0 + 63 > qbase[qb]) ||
+                       (SEG && (j0 < sw.ilo || j0 + 64 > sw.ihi)))) {
             asm volatile("");
             mask_block(qb);
           }
+        }
+        if (!PAIR && ((j0 + 64 > N) || (CAUSAL && j0 + 63 > qbase[0]) ||
+                      (SEG && (j0 < sw.ilo || j0 + 64 > sw.ihi)))) {
+          asm volatile("");
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mask_block(qb);
         }
       }
 
