@@ -253,7 +253,10 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
   // chunk is reversed.  Columns 0..63 are keys j0b.., 64..127 keys j0b + 64..
   // (PAIR: keys jrB..).  The loads of tile t + 1 are issued during tile t
   // (before that step's tile prefetch) and written at its end.
-  uint4 zr[2];
+  // (a tile that needs no Z^Q loads and stores none: its LDS copy is never
+  // read)
+  uint4 zr[2] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
+  bool zq_need = false;
   auto load_zq = [&](int t) {
     const int i0 = t * kT;
     const int jr0 = j0b, jr1 = PAIR ? jrB : j0b + 64;
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     const bool need = t < nqt && !(sat0 && sat1);
     // (a uniform branch: a tile saturated for both halves reads no Z^Q, and
     // out-of-range loads still cost; its LDS copy is then never read)
-    zr[0] = zr[1] = uint4{0, 0, 0, 0};
+    zq_need = need;
     if (!need) return;
     const GroupInfo gq = sload_uniform16(a.gq + i0 / kGroup);
     const int gq0s = (i0 / kGroup) * kGroup;
@@ -279,6 +282,7 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
     }
   };
   auto store_zq = [&](int buf) {
+    if (!zq_need) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + 256 * u;
