@@ -56,6 +56,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
   // (8% faster: see below); without one the Z^Q runs, then requested before
   // the products, cost more than that saves
   constexpr bool BAND_INIT = (F & F_ZK) != 0;
+  // band terms added to the scores as 4-vectors, so that the saturated and
+  // band branches merge the scores in register pairs (bias or key table: 2%
+  // faster; query table alone: 3% slower, the scalar adds stay)
+  constexpr bool VEC_ADD = (F & (F_ZK | F_BT)) != 0;
   using GT = std::conditional_t<(F & F_DZ16) != 0, _Float16,
                                 typename DzType<bf16, (F & F_DZ32) != 0>::type>;
   // key projections of a band tile are staged into LDS once per workgroup
@@ -429,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
           halfx4 zk4 = halfx4{0, 0, 0, 0};
           if (STZK)  // Z^K[j1 + t][i - j1 - t + D], t = 0..3 (the lane's base, plus rows 16 kb and the block's columns)
             zk4 = __builtin_bit_cast(halfx4, lds_tr4_at(szk_lane + (16 * kb) * kZP + (qbase[qb] - i0)));
+          floatx4 add4;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int j = j1 + t;
@@ -436,18 +441,18 @@ __global__ __launch_bounds__(256, 2) void bwd_q_fast(AttnArgs a, int nqb, int to
             float band = km[t] + zq[t];
             if (F & F_ZK) band += static_cast<float>(zk4[t]);
             if (F & F_BT) band += bloadf(rbt, static_cast<uint32_t>(iclamp(dl + D, 0, 2 * D) * 4));
-            float add;
             if constexpr (PURE) {
-              add = band;
+              add4[t] = band;
             } else {
               const float kedge = KC3 ? (dl >= D ? khi4[t] : klo4[t]) : km[t];
-              add = dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
+              add4[t] = dl >= D ? (rhi[qb] + kedge) : (dl <= -D ? (rlo[qb] + kedge) : band);
             }
-            if constexpr (ASSIGN)
-              s[qb][kb][t] = add;  // the initial value of the accumulator
-            else
-              s[qb][kb][t] += add;
+            if constexpr (!ASSIGN && !VEC_ADD) s[qb][kb][t] += add4[t];
           }
+          if constexpr (ASSIGN)
+            s[qb][kb] = add4;  // the initial value of the accumulator
+          else if constexpr (VEC_ADD)
+            s[qb][kb] += add4;
           // keep each 4-run's loads next to their use (register pressure)
           __builtin_amdgcn_sched_barrier(0);
         }
