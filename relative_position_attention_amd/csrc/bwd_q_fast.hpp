@@ -5,8 +5,11 @@
 // A workgroup of 4 waves owns 128 queries (one projection group), 32 per
 // wave.  Key tiles of 64 keys (K, V row-major; per-key boundary entries)
 // stream through double-buffered LDS.  Per tile and wave the pass rebuilds
-// the scores exactly as the forward does (same relation terms, same
-// boundary-entry rule) and, from the saved logsumexp L and D = rowdot(dO, O)
+// the scores as the forward does (same relation terms, same boundary-entry
+// rule; the band terms enter as the S accumulator's initial value with a key
+// table, else after the products, so without one a band score may differ
+// from the forward's in its last bit) and, from the saved logsumexp L and
+// D = rowdot(dO, O)
 // ([RPA] §3.1 Eq. (3), App. B tile-locality lemma):
 //   S^T = K Q^T and dP^T = V dO^T on MFMA (A from LDS rows, B in registers),
 //   P = exp2(S tau log2 e - L log2 e), G' = P (dP - D) (the gradient of the

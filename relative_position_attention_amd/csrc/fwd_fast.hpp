@@ -4,8 +4,9 @@
 //
 // Layout.  A workgroup of 4 waves owns 128 consecutive queries (one
 // projection group); each wave owns 32 of them (two 16-query blocks), which
-// keeps a wave within 128 registers so four workgroups share a CU and the
-// MFMA work of some waves overlaps the softmax of others.  Key tiles of 64
+// keeps a wave within 168 registers so three workgroups share a CU (two
+// with a key table, causal pairing or in-tile products) and the MFMA work
+// of some waves overlaps the softmax of others.  Key tiles of 64
 // keys stream through LDS, double buffered: K and V row-major (the V^T
 // operand of P V is read with the gfx950 transposing LDS read), and (when a
 // per-key relation term exists) the tile's per-key boundary entries.
@@ -17,7 +18,9 @@
 //   satisfy delta >= D or delta <= -D is saturated and adds one fp32 entry per
 //   query (folded into the exponent's offset) and one per key (the initial
 //   value of the S accumulator); band tiles
-//   read the per-pair projections Z ([RPA] §4.1, App. B saturated-tile lemma).
+//   read the per-pair projections Z ([RPA] §4.1, App. B saturated-tile lemma),
+//   which without causal pairing are the S accumulator's initial value too
+//   (with it, and for in-tile products, they are added after the products).
 //   Every pair with |delta| >= D takes the boundary entries whatever its tile,
 //   exactly as the backward passes do.
 //   Online softmax in base 2 with tau log2(e) folded into one FMA ([RPA]

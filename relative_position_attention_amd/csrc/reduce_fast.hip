@@ -467,8 +467,8 @@ __global__ __launch_bounds__(256) void partials_fast(PartialArgs p) {
   if (want_p2) {
 #pragma unroll
     for (int st = 0; st < W; ++st) p2red[tid >> 6][64 * st + (tid & 63)] = p2acc[st];
-    // (bred is free again: its last reads precede the P1 epilogue's writes
-    // of the partials, or it was never used)
+    // (bred is free again: its only readers in the P1 epilogue are these
+    // same threads, which read it before they write it here)
     if ((has0 || has2) && tid < 64) {
       bred[0][0][tid] = bs0;
       bred[0][1][tid] = bs1;
