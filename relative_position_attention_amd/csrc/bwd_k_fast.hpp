@@ -539,7 +539,20 @@ __global__ __launch_bounds__(256, 2) void bwd_k_fast(AttnArgs a, int nkb, int to
       }
 
       // key offset gradients and column sums
-      if (DZ || CS) {
+      if (DZ && !CS && !PAIR && (sat_lo[0] || sat_hi[0])) {
+        // a saturated tile (both blocks: without pairing they share the
+        // wave's range): every key's sum of G' goes to one boundary entry,
+        // one uniform branch instead of a three-way branch per block
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const float g0 = (dp[0][kb][0] + dp[0][kb][1]) + (dp[0][kb][2] + dp[0][kb][3]);
+          const float g1 = (dp[1][kb][0] + dp[1][kb][1]) + (dp[1][kb][2] + dp[1][kb][3]);
+          if (sat_lo[0])
+            blo[kb] += g0 + g1;
+          else
+            bhi[kb] += g0 + g1;
+        }
+      } else if (DZ || CS) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb == 1 && !both) continue;
