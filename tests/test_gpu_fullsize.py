@@ -93,6 +93,18 @@ def test_bench_shape(name):
     _compare(_problem(spec, arr), got, slices, heads, f"bench-{name}")
 
 
+@pytest.mark.parametrize("name", ["shaw", "deberta"])
+def test_bench_shape_bf16_outputs(name):
+    # the descriptor's bf16 output mode (O, dQ, dK, dV stored in bf16, D
+    # taken from the rounded O) at the bench's full size, against the oracle
+    # at the bf16 tolerances
+    spec, arr = make_problem(**BENCH_SHAPES[name])
+    print(f"[full] bench {name} bf16 outputs B={spec['B']} H={spec['H']} N={spec['N']}", flush=True)
+    got = run_library(spec, arr, out_dtype="bf16")
+    slices, heads = ([(0, 2), (1, 2)], [2]) if name == "deberta" else ([(1, 9)], [])
+    _compare(_problem(spec, arr), got, slices, heads, f"bench-{name}-bf16out")
+
+
 def test_bench_shaw_table_gradient():
     # the Shaw table is shared by all heads: its gradient sums every slice, so
     # it is checked whole on a one-slice problem of the bench's map and length
