@@ -93,7 +93,7 @@ def test_bench_shape(name):
     _compare(_problem(spec, arr), got, slices, heads, f"bench-{name}")
 
 
-@pytest.mark.parametrize("name", ["shaw", "deberta"])
+@pytest.mark.parametrize("name", ["shaw", "deberta", "txl"])
 def test_bench_shape_bf16_outputs(name):
     # the descriptor's bf16 output mode (O, dQ, dK, dV stored in bf16, D
     # taken from the rounded O) at the bench's full size, against the oracle
@@ -101,7 +101,7 @@ def test_bench_shape_bf16_outputs(name):
     spec, arr = make_problem(**BENCH_SHAPES[name])
     print(f"[full] bench {name} bf16 outputs B={spec['B']} H={spec['H']} N={spec['N']}", flush=True)
     got = run_library(spec, arr, out_dtype="bf16")
-    slices, heads = ([(0, 2), (1, 2)], [2]) if name == "deberta" else ([(1, 9)], [])
+    slices, heads = {"deberta": ([(0, 2), (1, 2)], [2]), "txl": ([(0, 5)], [5])}.get(name, ([(1, 9)], []))
     _compare(_problem(spec, arr), got, slices, heads, f"bench-{name}-bf16out")
 
 
