@@ -22,5 +22,6 @@ themselves they are "parity unpinned".
 """
 
 from .maps import t5_bucket, log_bucket, map_rows, relation_rows  # noqa: F401
-from .attention import forward, backward, forward_backward, slice_forward_backward  # noqa: F401
+from .attention import (forward, backward, forward_backward, slice_forward_backward,  # noqa: F401
+                        query_rows)
 from .bruteforce import brute_forward_backward  # noqa: F401

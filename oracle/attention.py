@@ -45,7 +45,7 @@ by all heads).  Everything is float64.
 
 import numpy as np
 
-from .maps import relation_rows
+from .maps import map_rows, relation_rows
 from .philox import keep_mask, keep_scale
 
 
@@ -190,6 +190,63 @@ def slice_forward_backward(spec, arrays, b, h, rows=None):
     out["dq"] = dq
     out["dk"] = dk
     return out
+
+
+def query_rows(spec, arrays, b, h, qidx):
+    """O, L and dQ of the query rows ``qidx`` of slice (b, h), for sequences
+    too long for the N x N slice.  The same definitions as
+    ``slice_forward_backward``, evaluated on those rows only: a row's
+    softmax, its D_i = <dO_i, O_i> and dQ_i = sum_j G_ij k_j + sum_r
+    dZ^Q[i, r] A^Q[r] involve that row alone ([RPA] App. B.1).  Without
+    segment masks or dropout."""
+    assert spec.get("segments") is None and spec.get("dropout") is None
+    N = spec["N"]
+    tau = float(spec["scale"])
+    qidx = np.asarray(qidx, dtype=np.int64)
+    n = qidx.size
+    jdx = np.arange(N, dtype=np.int64)
+    delta = qidx[:, None] - jdx[None, :]
+    masked = delta < 0 if spec["causal"] else np.zeros_like(delta, dtype=bool)
+
+    def rho(term):
+        r = map_rows(spec["map"], spec["signs"][term] * delta)
+        r[masked] = 0  # masked pairs contribute nothing; any valid row serves
+        return r
+
+    q = arrays["q"][b, h][qidx]
+    k = arrays["k"][b, h]
+    v = arrays["v"][b, h]
+    do = arrays["do"][b, h][qidx]
+    s = (q + arrays["u"][h] if _has(spec, "u") else q) @ k.T
+    if _has(spec, "aq"):
+        a = _aq(spec, arrays, h)
+        rq = rho("aq")
+        qp = q + arrays["v_bias"][h] if _has(spec, "v") else q
+        s += np.take_along_axis(qp @ a.T, rq, axis=1)
+    if _has(spec, "ak"):
+        zk = k @ arrays["ak"][:, h, :].T  # Z^K [N, R]
+        s += zk[jdx[None, :], rho("ak")]  # Z^K[j, phi_K(i, j)]
+    if _has(spec, "bias"):
+        s += arrays["bias"][:, h][rho("bias")]
+    s *= tau
+    s[masked] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m)
+    ssum = e.sum(axis=1, keepdims=True)
+    p = e / np.where(ssum > 0, ssum, 1.0)
+    o = p @ v
+    with np.errstate(divide="ignore"):
+        lse = (m + np.log(ssum))[:, 0]
+    dd = np.sum(do * o, axis=1, keepdims=True)
+    g = tau * p * (do @ v.T - dd)
+    dq = g @ k
+    if _has(spec, "aq"):
+        R = spec["rows"]
+        flat = (np.arange(n)[:, None] * R + rq).ravel()
+        dzq = np.bincount(flat, weights=g.ravel(), minlength=n * R).reshape(n, R)
+        dq += dzq @ a
+    return o, lse, dq
 
 
 def _empty_grads(spec):

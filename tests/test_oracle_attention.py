@@ -272,3 +272,33 @@ def test_noncontiguous_map_bruteforce(causal):
     got = oracle.forward_backward(spec, arr)
     for key in ref:
         np.testing.assert_allclose(got[key], ref[key], rtol=1e-10, atol=1e-12, err_msg=key)
+
+
+@pytest.mark.parametrize("kind,causal", CASES)
+def test_query_rows_match_bruteforce(kind, causal):
+    # the row-sampled oracle (for sequences too long for N x N) against the
+    # per-pair brute force: O, L and dQ of every row, in an order that is not
+    # the rows' own
+    spec, arr = tiny(kind, N=11, d=3, B=2, H=2, causal=causal, seed=9)
+    ref = oracle.brute_forward_backward(spec, arr)
+    rows = [10, 0, 5, 1, 9, 2, 8, 3, 7, 4, 6]
+    for b in range(2):
+        for h in range(2):
+            o, lse, dq = oracle.query_rows(spec, arr, b, h, rows)
+            np.testing.assert_allclose(o, ref["o"][b, h][rows], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(lse, ref["lse"][b, h][rows], rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(dq, ref["dq"][b, h][rows], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,causal", CASES)
+def test_query_rows_match_slices_real_maps(kind, causal):
+    # the same at the mechanisms' own maps and a length past their
+    # saturation radii (Shaw clip 16, T5 91, DeBERTa's log region), against
+    # the full-slice oracle
+    spec, arr = make_problem(kind, 1, 1, 300, "f32", 11, causal=causal, clip=16)
+    full = oracle.slice_forward_backward(spec, arr, 0, 0)
+    rows = [299, 0, 1, 150, 16, 17, 91, 92, 200, 298]
+    o, lse, dq = oracle.query_rows(spec, arr, 0, 0, rows)
+    np.testing.assert_allclose(o, full["o"][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, full["lse"][rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dq, full["dq"][rows], rtol=1e-10, atol=1e-12)
