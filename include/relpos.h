@@ -160,6 +160,9 @@ typedef struct relpos_desc {
   int32_t reserved0;       /* must be 0                                      */
 } relpos_desc;
 
+/* Problem shape: B, H >= 1, 1 <= N <= 2^22, d = 64.  An empty problem (any
+   of B, H, N zero) is refused with RELPOS_E_INVALID_ARG rather than treated
+   as a no-op; N > 2^22 and d != 64 are RELPOS_E_UNSUPPORTED. */
 typedef struct relpos_shape {
   int32_t B, H, N, d;
 } relpos_shape;

@@ -114,7 +114,10 @@ def test_validation_errors():
     spec = _spec_small(1, 128)
     assert _err(spec, d=32) == -2                      # head dim != 64: UNSUPPORTED
     assert _err(spec, abi_version=7) == -7             # ABI
-    assert _err(spec, N=0) == -1
+    assert _err(spec, N=0) == -1                       # empty problems are refused
+    assert _err(spec, B=0) == -1
+    assert _err(spec, H=0) == -1
+    assert _err(spec, N=(1 << 22) + 1) == -2          # longer than 2^22: UNSUPPORTED
     assert _err(spec, terms=1 << 7) == -1              # unknown term bit
     assert _err(spec, terms=16) == -1                  # V without AQ
     assert _err(spec, dtype=5) == -1
