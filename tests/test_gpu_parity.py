@@ -98,6 +98,22 @@ def test_saturated_tiles_small_delta():
     _case("shaw-D16-N1024", spec, arr)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("clip", [0, 1])
+def test_degenerate_clip(clip, dtype):
+    # the smallest saturation radii: clip 0 (one table row, no band at all,
+    # the two boundary rows 0 and 2D are the same row) and clip 1 (three
+    # rows, a band of one diagonal), for the query table alone and for the
+    # query and key tables with a bias, causal and not
+    for causal in (False, True):
+        spec, arr = make_problem(kind="shaw", B=1, H=2, N=200, dtype=dtype, seed=41 + clip,
+                                 causal=causal, clip=clip, shared_table=False)
+        _case(f"shaw-clip{clip}-{dtype}-c{int(causal)}", spec, arr)
+        spec, arr = make_mixed(["aq", "ak", "bias"], 1, 2, 200, dtype, 43 + clip, causal=causal,
+                               clip=clip)
+        _case(f"qkb-clip{clip}-{dtype}-c{int(causal)}", spec, arr)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_explicit_map(causal):
     # an explicit row table ([RPA] relation map as a lookup over clipped
