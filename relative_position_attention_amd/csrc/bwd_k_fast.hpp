@@ -40,7 +40,11 @@ namespace relpos {
 
 namespace {
 
-constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
+// tile pitch (bf16): 160-byte rows, a 40-dword stride that puts eight
+// consecutive rows on distinct 8-bank groups, so the transposing reads of
+// 16 rows (and the row reads of 8) meet no bank conflict (at 144 bytes two
+// of the eight rows shared banks)
+constexpr int kP = 80;
 constexpr int kT = 32;  // queries per tile
 constexpr int kKwP = 36;  // in-tile scratch pitch (fp32): 32 window rows
 

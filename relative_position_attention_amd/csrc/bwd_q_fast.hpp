@@ -37,7 +37,10 @@ namespace relpos {
 
 namespace {
 
-constexpr int kP = 72;  // tile pitch (bf16): 144-byte rows
+// tile pitch (bf16): 160-byte rows, a 40-dword stride that puts eight
+// consecutive rows on distinct 8-bank groups (no bank conflict in the
+// transposing reads; 144 bytes had two rows of eight sharing banks)
+constexpr int kP = 80;
 // in-tile scratch pitch (fp32): 80 window rows, or a G' row with its zero
 // margins (32 + 64 + 16 entries)
 constexpr int kQwP = 116;

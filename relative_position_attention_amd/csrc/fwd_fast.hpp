@@ -53,7 +53,7 @@ namespace {
 constexpr int QB = 2;              // 16-query blocks per wave
 constexpr int kWQ = 16 * QB;       // queries per wave
 constexpr int kBM = 4 * kWQ;       // queries per workgroup
-constexpr int kKP = 72;            // K and V tile pitch (bf16): 144-byte rows
+constexpr int kKP = 80;            // K and V tile pitch (bf16): 160-byte rows (bank-conflict free)
 constexpr float kLazy = 8.f;       // rescale threshold, log2 units
 constexpr int kZwP = 84;           // in-tile scratch pitch (fp32): 80 window rows
 // an MFMA A operand whose 16 rows are all ones (bf16 1.0 = 0x3f80)
